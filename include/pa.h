@@ -1,0 +1,162 @@
+/*
+ * pa.h -- C ABI of the paged-KV attention step for AMD MI355X (gfx950).
+ *
+ * The step is the attention layer's work per decoder layer in a paged-KV inference engine: write the new
+ * tokens' K/V into a block-paged cache, then run attention over that cache through per-sequence block tables,
+ * either as variable-length causal prefill or as one-query-per-sequence decode ("一个 prompt 的一生" §3.3.2 and
+ * the summary of §4: store_kvcache, then flash_attn; "Nano-vLLM 架构详解" §2.4, Attention stage, and §3.2,
+ * Attention 运算 for the argument formats).
+ *
+ * Conventions shared by every entry point
+ *   - Pointers marked (device) are HIP device pointers; (host) are host pointers. The caller owns every buffer.
+ *     The library allocates nothing, keeps no per-call state and may be called from several host threads.
+ *   - Every call only enqueues work on `stream` (a hipStream_t, NULL = the default stream) and returns; it does
+ *     not synchronise and reads no device memory on the host. Grids depend only on host scalars, so a captured
+ *     graph can be replayed with new lengths and tables as long as those scalars stay the same.
+ *   - Cache of one layer, for K and for V separately: [num_blocks, block_size, num_kv_heads, head_dim],
+ *     contiguous ("一个 prompt 的一生" §2.2.3, the pool `torch.empty(2, num_layers, num_blocks, block_size,
+ *     num_kv_heads, head_dim)` whose per-layer views are handed to the layer). Because it is contiguous in
+ *     (block, offset), a slot s = block_id * block_size + offset addresses row s of a flat
+ *     [num_blocks * block_size, num_kv_heads, head_dim] view ("Nano-vLLM 架构详解" §1, Step2).
+ *   - Index arrays are int32. A block table is [batch, max_blocks_per_seq], row s listing sequence s's physical
+ *     blocks in logical order, padded with -1 ("Nano-vLLM 架构详解" §3.2, block_tables format). Only the first
+ *     ceil(k_len / block_size) entries of a row are read.
+ *   - Query head h reads KV head h / (num_heads / num_kv_heads) (contiguous GQA groups).
+ *   - A query token at absolute position p sees keys 0..p. In prefill, the q_len new tokens of a sequence with
+ *     k_len keys are at positions k_len - q_len .. k_len - 1 (a chunk continues at the number of cached tokens,
+ *     "Nano-vLLM 源码逐行解析 第2篇", sequence.py counter example).
+ *   - Attention inputs are read from the cache only: call pa_store_kvcache for the new tokens first.
+ *   - Device-side indices are trusted: out-of-range block ids or slots, duplicate slots within one store and
+ *     k_len < q_len are undefined behaviour. Cache contents outside each sequence's first k_len positions are
+ *     never read, so they may hold any bits (NaN included).
+ *   - Return value: PA_OK, or an error code for a problem the host can see before launching (nothing is
+ *     launched then); PA_ERR_LAUNCH if a launch failed. batch == 0 or no tokens is a no-op returning PA_OK.
+ *
+ * Supported: dtype PA_BF16 or PA_F32 for Q/K/V and cache (same for all); out_dtype PA_F32 or PA_BF16
+ * (round to nearest even); head_dim a multiple of 8 and at most 256 (bf16, head_dim 128 and a GQA group of at
+ * most 16 take the matrix-core kernels; other shapes take a plain vector kernel).
+ */
+#ifndef PA_H_
+#define PA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  PA_OK = 0,
+  PA_ERR_NULL = 1,        /* a required pointer is NULL */
+  PA_ERR_SHAPE = 2,       /* inconsistent sizes (e.g. num_heads % num_kv_heads != 0, negative sizes) */
+  PA_ERR_UNSUPPORTED = 3, /* dtype / head_dim combination not built */
+  PA_ERR_WORKSPACE = 4,   /* workspace smaller than the *_workspace_bytes query asks for */
+  PA_ERR_LAUNCH = 5       /* the HIP runtime reported an error when launching */
+} pa_status;
+
+typedef enum { PA_F32 = 0, PA_BF16 = 1 } pa_dtype;
+
+/* Human-readable name of a status code (static string). */
+const char* pa_status_str(pa_status s);
+
+/* Library version: major * 10000 + minor * 100 + patch. */
+int pa_version(void);
+
+/*
+ * pa_build_metadata -- per-step metadata of the paged cache, computed on the device.
+ *
+ * Sequence s computes num_new[s] tokens at absolute positions num_cached[s] .. num_cached[s] + num_new[s] - 1,
+ * after which it has k_len = num_cached[s] + num_new[s] keys. Outputs (device, int32):
+ *   cu_seqlens_q [batch+1]  prefix sums of num_new (cu_seqlens_q[0] = 0)
+ *   cu_seqlens_k [batch+1]  prefix sums of k_len
+ *   context_lens [batch]    k_len
+ *   positions    [total_q]  absolute position of each flattened new token
+ *   slot_mapping [total_q]  block_table[s][pos / block_size] * block_size + pos % block_size
+ * This is the flattening of the prepare_prefill example ("一个 prompt 的一生" §3.3.2: positions, cu_seqlens_q and
+ * slot_mapping for two sequences with block_size 4) and the slot formula ("Nano-vLLM 架构详解" §1, Step2). For
+ * a decode step pass num_new = 1 for every sequence.
+ * total_q (host) must equal sum(num_new); batch <= 4096; num_blocks * block_size < 2^31.
+ * Inputs num_cached, num_new [batch] and block_table [batch, max_blocks_per_seq] are device pointers.
+ */
+pa_status pa_build_metadata(const int32_t* num_cached, const int32_t* num_new, const int32_t* block_table,
+                            int32_t max_blocks_per_seq, int32_t batch, int32_t total_q, int32_t num_blocks,
+                            int32_t block_size, int32_t* cu_seqlens_q, int32_t* cu_seqlens_k,
+                            int32_t* context_lens, int32_t* positions, int32_t* slot_mapping, void* stream);
+
+/*
+ * pa_store_kvcache -- write each new token's K and V into the cache at its slot.
+ *
+ * For every token i < num_tokens with slot_mapping[i] >= 0: flat_k_cache[slot_mapping[i]] = k[i] and
+ * flat_v_cache[slot_mapping[i]] = v[i] (a bit copy of num_kv_heads * head_dim elements). Negative slots are
+ * skipped. The write knows nothing about pages: it only follows slot_mapping ("一个 prompt 的一生" §3.3.2 and
+ * §4; "Nano-vLLM 架构详解" §3.2, KV cache 写入函数).
+ *   k, v        (device) [num_tokens, num_kv_heads, head_dim]; token i starts at element i * *_tok_stride and
+ *               its num_kv_heads * head_dim elements are contiguous
+ *   k_cache, v_cache (device) [num_blocks, block_size, num_kv_heads, head_dim]
+ *   slot_mapping (device) [num_tokens]
+ */
+pa_status pa_store_kvcache(const void* k, int64_t k_tok_stride, const void* v, int64_t v_tok_stride,
+                           void* k_cache, void* v_cache, const int32_t* slot_mapping, int32_t num_tokens,
+                           int32_t num_kv_heads, int32_t head_dim, int32_t num_blocks, int32_t block_size,
+                           pa_dtype dtype, void* stream);
+
+/*
+ * pa_prefill_varlen -- causal attention of the new tokens of `batch` sequences over the paged cache.
+ *
+ * For sequence s, rows cu_seqlens_q[s] .. cu_seqlens_q[s+1]-1 of q attend to its
+ * k_len = cu_seqlens_k[s+1] - cu_seqlens_k[s] keys read through block_table row s, with
+ * O = softmax(q K^T * softmax_scale + causal mask) V computed with float32 accumulation. Argument formats are
+ * FlashAttention's varlen ones ("Nano-vLLM 架构详解" §3.2, Attention 运算: Q (total_q, nheads, headdim), cache
+ * (num_blocks, page_block_size, nheads_k, headdim), cu_seqlens (batch+1,), max_seqlen, block_tables).
+ *   q            (device) [total_q, num_heads, head_dim]; token i starts at element i * q_tok_stride
+ *   cu_seqlens_q, cu_seqlens_k (device) [batch+1]
+ *   block_table  (device) [batch, max_blocks_per_seq]
+ *   max_seqlen_q (host) >= every q_len; max_seqlen_k (host) >= every k_len (sizes the grid)
+ *   out          (device) [total_q, num_heads, head_dim], contiguous, out_dtype
+ *   workspace    (device) at least pa_prefill_workspace_bytes(...) bytes (may be NULL when that is 0)
+ */
+pa_status pa_prefill_varlen(const void* q, int64_t q_tok_stride, const void* k_cache, const void* v_cache,
+                            const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, const int32_t* block_table,
+                            int32_t max_blocks_per_seq, int32_t batch, int32_t total_q, int32_t max_seqlen_q,
+                            int32_t max_seqlen_k, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                            int32_t num_blocks, int32_t block_size, float softmax_scale, pa_dtype dtype,
+                            void* out, pa_dtype out_dtype, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes pa_prefill_varlen needs for these host sizes (currently always 0). */
+size_t pa_prefill_workspace_bytes(int32_t batch, int32_t num_heads, int32_t head_dim, int32_t max_seqlen_q,
+                                  int32_t max_seqlen_k);
+
+/*
+ * pa_decode -- one query token per sequence over its context_lens[s] cached keys (the new token included).
+ *
+ * Same arithmetic as prefill with q_len = 1 (the query at position context_lens[s] - 1 sees every key). The
+ * keys are cut into splits of split_tokens; each split yields an unnormalised partial output with its running
+ * max and sum, and a second pass merges the partials of a sequence with the log-sum-exp rule. FlashAttention's
+ * KV-cache format: q (batch, 1, nheads, headdim), cache_seqlens, block_tables ("Nano-vLLM 架构详解" §3.2).
+ *   q            (device) [batch, num_heads, head_dim]; sequence s starts at element s * q_tok_stride
+ *   context_lens (device) [batch], each >= 1 and <= max_blocks_per_seq * block_size
+ *   block_table  (device) [batch, max_blocks_per_seq]
+ *   split_tokens (host) keys per split, a multiple of 32, or 0 to let the library choose from the host sizes
+ *   out          (device) [batch, num_heads, head_dim], contiguous, out_dtype
+ *   workspace    (device) at least pa_decode_workspace_bytes(...) bytes for the same host sizes
+ */
+pa_status pa_decode(const void* q, int64_t q_tok_stride, const void* k_cache, const void* v_cache,
+                    const int32_t* context_lens, const int32_t* block_table, int32_t max_blocks_per_seq,
+                    int32_t batch, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim, int32_t num_blocks,
+                    int32_t block_size, float softmax_scale, pa_dtype dtype, void* out, pa_dtype out_dtype,
+                    int32_t split_tokens, void* workspace, size_t workspace_bytes, void* stream);
+
+/* Keys per split pa_decode uses for these host sizes when split_tokens == 0. */
+int32_t pa_decode_split_tokens(int32_t batch, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                               int32_t max_blocks_per_seq, int32_t block_size);
+
+/* Workspace bytes pa_decode needs for these host sizes and split_tokens (0 = the library's choice). */
+size_t pa_decode_workspace_bytes(int32_t batch, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                                 int32_t max_blocks_per_seq, int32_t block_size, int32_t split_tokens);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H_ */

@@ -1,0 +1,23 @@
+"""Paged-KV attention step for AMD MI355X (gfx950): store_kvcache, varlen causal prefill and split-K decode over
+a block-paged cache, as hand-written HIP kernels behind a C ABI (include/pa.h, libpa.so).
+
+The Python functions below only marshal torch tensors into the C calls; see binding.py.
+"""
+
+from .binding import (  # noqa: F401
+    PAError,
+    build_metadata,
+    decode,
+    decode_split_tokens,
+    decode_workspace_bytes,
+    lib,
+    prefill_varlen,
+    prefill_workspace_bytes,
+    status_str,
+    store_kvcache,
+)
+
+__all__ = [
+    "PAError", "build_metadata", "decode", "decode_split_tokens", "decode_workspace_bytes", "lib",
+    "prefill_varlen", "prefill_workspace_bytes", "status_str", "store_kvcache",
+]

@@ -1,0 +1,199 @@
+// The C ABI: argument checks on the host, kernel choice, launch. No allocation, no synchronisation, no reads of
+// device memory; every error that the host can see is returned before anything is launched.
+#include "../../include/pa.h"
+#include "pa_launch.h"
+
+namespace {
+
+constexpr int kVersion = 100;  // 0.1.0
+constexpr int64_t kInt32Max = 2147483647;
+
+bool aligned(const void* p, int bytes) { return (reinterpret_cast<uintptr_t>(p) % uintptr_t(bytes)) == 0; }
+
+bool valid_dtype(pa_dtype d) { return d == PA_F32 || d == PA_BF16; }
+
+int elem_bytes(pa_dtype d) { return d == PA_BF16 ? 2 : 4; }
+
+bool valid_head_dim(int32_t d) { return d > 0 && d <= 256 && d % 8 == 0; }
+
+pa_status launched() { return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_LAUNCH; }
+
+// Keys per decode split chosen from host sizes only: about 32k work items for contexts at half the table's
+// capacity, clamped to [256, 4096] keys and rounded to a power of two (a multiple of 32).
+int32_t auto_split(int32_t batch, int32_t num_kv_heads, int32_t mbps, int32_t block_size) {
+  const int64_t max_len = int64_t(mbps) * block_size;
+  const int64_t head_keys = int64_t(batch) * num_kv_heads * (max_len / 2 + 1);
+  int64_t want = head_keys / 32768;
+  int32_t split = 256;
+  while (split < 4096 && split < want) split *= 2;
+  return split;
+}
+
+int32_t max_splits_for(int32_t mbps, int32_t block_size, int32_t split) {
+  const int64_t max_len = int64_t(mbps) * block_size;
+  return int32_t((max_len + split - 1) / split);
+}
+
+bool decode_uses_mfma(pa_dtype dtype, int32_t Hq, int32_t Hkv, int32_t D) {
+  return dtype == PA_BF16 && D == 128 && Hq / Hkv <= 16;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* pa_status_str(pa_status s) {
+  switch (s) {
+    case PA_OK: return "PA_OK";
+    case PA_ERR_NULL: return "PA_ERR_NULL: a required pointer is NULL";
+    case PA_ERR_SHAPE: return "PA_ERR_SHAPE: inconsistent sizes";
+    case PA_ERR_UNSUPPORTED: return "PA_ERR_UNSUPPORTED: dtype or head_dim not supported";
+    case PA_ERR_WORKSPACE: return "PA_ERR_WORKSPACE: workspace too small";
+    case PA_ERR_LAUNCH: return "PA_ERR_LAUNCH: kernel launch failed";
+  }
+  return "unknown pa_status";
+}
+
+int pa_version(void) { return kVersion; }
+
+pa_status pa_build_metadata(const int32_t* num_cached, const int32_t* num_new, const int32_t* block_table,
+                            int32_t max_blocks_per_seq, int32_t batch, int32_t total_q, int32_t num_blocks,
+                            int32_t block_size, int32_t* cu_seqlens_q, int32_t* cu_seqlens_k,
+                            int32_t* context_lens, int32_t* positions, int32_t* slot_mapping, void* stream) {
+  if (batch < 0 || batch > 4096 || total_q < 0 || block_size <= 0 || num_blocks <= 0) return PA_ERR_SHAPE;
+  if (int64_t(num_blocks) * block_size > kInt32Max) return PA_ERR_SHAPE;
+  if (batch == 0) return total_q == 0 ? PA_OK : PA_ERR_SHAPE;
+  if (max_blocks_per_seq <= 0) return PA_ERR_SHAPE;
+  if (!num_cached || !num_new || !block_table || !cu_seqlens_q || !cu_seqlens_k || !context_lens)
+    return PA_ERR_NULL;
+  if (total_q > 0 && (!positions || !slot_mapping)) return PA_ERR_NULL;
+  pa::launch_build_metadata(num_cached, num_new, block_table, max_blocks_per_seq, batch, total_q, block_size,
+                            cu_seqlens_q, cu_seqlens_k, context_lens, positions, slot_mapping,
+                            static_cast<hipStream_t>(stream));
+  return launched();
+}
+
+pa_status pa_store_kvcache(const void* k, int64_t k_tok_stride, const void* v, int64_t v_tok_stride,
+                           void* k_cache, void* v_cache, const int32_t* slot_mapping, int32_t num_tokens,
+                           int32_t num_kv_heads, int32_t head_dim, int32_t num_blocks, int32_t block_size,
+                           pa_dtype dtype, void* stream) {
+  if (!valid_dtype(dtype)) return PA_ERR_UNSUPPORTED;
+  if (num_tokens < 0 || num_kv_heads <= 0 || head_dim <= 0 || num_blocks <= 0 || block_size <= 0)
+    return PA_ERR_SHAPE;
+  if (int64_t(num_blocks) * block_size > kInt32Max) return PA_ERR_SHAPE;
+  const int64_t row = int64_t(num_kv_heads) * head_dim;
+  if (k_tok_stride < row || v_tok_stride < row) return PA_ERR_SHAPE;
+  if (num_tokens == 0) return PA_OK;
+  if (!k || !v || !k_cache || !v_cache || !slot_mapping) return PA_ERR_NULL;
+  const int eb = elem_bytes(dtype);
+  const int64_t row_bytes = row * eb;
+  const int64_t ksb = k_tok_stride * eb, vsb = v_tok_stride * eb;
+  int vec = 16;
+  while (vec > eb && (row_bytes % vec || ksb % vec || vsb % vec || !aligned(k, vec) || !aligned(v, vec) ||
+                      !aligned(k_cache, vec) || !aligned(v_cache, vec)))
+    vec >>= 1;
+  if (row_bytes % vec || !aligned(k, vec) || !aligned(v, vec) || !aligned(k_cache, vec) || !aligned(v_cache, vec))
+    return PA_ERR_SHAPE;  // misaligned element pointers
+  pa::launch_store_kvcache(k, ksb, v, vsb, k_cache, v_cache, slot_mapping, num_tokens, row_bytes, vec,
+                           static_cast<hipStream_t>(stream));
+  return launched();
+}
+
+size_t pa_prefill_workspace_bytes(int32_t batch, int32_t num_heads, int32_t head_dim, int32_t max_seqlen_q,
+                                  int32_t max_seqlen_k) {
+  (void)batch; (void)num_heads; (void)head_dim; (void)max_seqlen_q; (void)max_seqlen_k;
+  return 0;
+}
+
+pa_status pa_prefill_varlen(const void* q, int64_t q_tok_stride, const void* k_cache, const void* v_cache,
+                            const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, const int32_t* block_table,
+                            int32_t max_blocks_per_seq, int32_t batch, int32_t total_q, int32_t max_seqlen_q,
+                            int32_t max_seqlen_k, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                            int32_t num_blocks, int32_t block_size, float softmax_scale, pa_dtype dtype,
+                            void* out, pa_dtype out_dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!valid_dtype(dtype) || !valid_dtype(out_dtype) || !valid_head_dim(head_dim)) return PA_ERR_UNSUPPORTED;
+  if (batch < 0 || total_q < 0 || num_heads <= 0 || num_kv_heads <= 0 || num_heads % num_kv_heads != 0 ||
+      block_size <= 0 || num_blocks <= 0 || max_seqlen_q < 0 || max_seqlen_k < 0)
+    return PA_ERR_SHAPE;
+  if (int64_t(num_blocks) * block_size > kInt32Max) return PA_ERR_SHAPE;
+  if (q_tok_stride < int64_t(num_heads) * head_dim) return PA_ERR_SHAPE;
+  if (batch == 0 || total_q == 0) return PA_OK;
+  if (max_seqlen_q <= 0 || max_blocks_per_seq <= 0 || int64_t(max_seqlen_k) > int64_t(max_blocks_per_seq) * block_size)
+    return PA_ERR_SHAPE;
+  if (!q || !k_cache || !v_cache || !cu_seqlens_q || !cu_seqlens_k || !block_table || !out) return PA_ERR_NULL;
+  if (workspace_bytes < pa_prefill_workspace_bytes(batch, num_heads, head_dim, max_seqlen_q, max_seqlen_k))
+    return PA_ERR_WORKSPACE;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const bool out_bf16 = out_dtype == PA_BF16;
+  const bool mfma = dtype == PA_BF16 && head_dim == 128 && q_tok_stride % 8 == 0 && aligned(q, 16) &&
+                    aligned(k_cache, 16) && aligned(v_cache, 16) && aligned(out, 16);
+  if (mfma) {
+    pa::launch_prefill_mfma(q, q_tok_stride, k_cache, v_cache, cu_seqlens_q, cu_seqlens_k, block_table,
+                            max_blocks_per_seq, batch, max_seqlen_q, num_heads, num_kv_heads, block_size,
+                            softmax_scale, out, out_bf16, st);
+  } else {
+    pa::launch_attn_generic(dtype == PA_BF16, q, q_tok_stride, k_cache, v_cache, cu_seqlens_q, cu_seqlens_k,
+                            nullptr, block_table, max_blocks_per_seq, batch, total_q, num_heads, num_kv_heads,
+                            head_dim, block_size, softmax_scale, out, out_bf16, st);
+  }
+  return launched();
+}
+
+int32_t pa_decode_split_tokens(int32_t batch, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                               int32_t max_blocks_per_seq, int32_t block_size) {
+  (void)num_heads; (void)head_dim;
+  if (batch <= 0 || num_kv_heads <= 0 || max_blocks_per_seq <= 0 || block_size <= 0) return 256;
+  return auto_split(batch, num_kv_heads, max_blocks_per_seq, block_size);
+}
+
+size_t pa_decode_workspace_bytes(int32_t batch, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                                 int32_t max_blocks_per_seq, int32_t block_size, int32_t split_tokens) {
+  if (batch <= 0 || num_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || max_blocks_per_seq <= 0 ||
+      block_size <= 0 || split_tokens < 0)
+    return 0;
+  const int32_t split = split_tokens > 0 ? split_tokens
+                                         : auto_split(batch, num_kv_heads, max_blocks_per_seq, block_size);
+  const int32_t ms = max_splits_for(max_blocks_per_seq, block_size, split);
+  if (ms <= 1) return 0;
+  return size_t(batch) * num_heads * ms * (size_t(head_dim) * sizeof(float) + 2 * sizeof(float));
+}
+
+pa_status pa_decode(const void* q, int64_t q_tok_stride, const void* k_cache, const void* v_cache,
+                    const int32_t* context_lens, const int32_t* block_table, int32_t max_blocks_per_seq,
+                    int32_t batch, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim, int32_t num_blocks,
+                    int32_t block_size, float softmax_scale, pa_dtype dtype, void* out, pa_dtype out_dtype,
+                    int32_t split_tokens, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!valid_dtype(dtype) || !valid_dtype(out_dtype) || !valid_head_dim(head_dim)) return PA_ERR_UNSUPPORTED;
+  if (batch < 0 || num_heads <= 0 || num_kv_heads <= 0 || num_heads % num_kv_heads != 0 || block_size <= 0 ||
+      num_blocks <= 0 || split_tokens < 0 || split_tokens % 32 != 0)
+    return PA_ERR_SHAPE;
+  if (int64_t(num_blocks) * block_size > kInt32Max) return PA_ERR_SHAPE;
+  if (q_tok_stride < int64_t(num_heads) * head_dim) return PA_ERR_SHAPE;
+  if (batch == 0) return PA_OK;
+  if (max_blocks_per_seq <= 0 || batch > 65535) return PA_ERR_SHAPE;
+  if (!q || !k_cache || !v_cache || !context_lens || !block_table || !out) return PA_ERR_NULL;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const bool out_bf16 = out_dtype == PA_BF16;
+  const bool mfma = decode_uses_mfma(dtype, num_heads, num_kv_heads, head_dim) && q_tok_stride % 8 == 0 &&
+                    aligned(q, 16) && aligned(k_cache, 16) && aligned(v_cache, 16) && aligned(out, 16);
+  if (mfma) {
+    const int32_t split = split_tokens > 0 ? split_tokens
+                                           : auto_split(batch, num_kv_heads, max_blocks_per_seq, block_size);
+    const int32_t ms = max_splits_for(max_blocks_per_seq, block_size, split);
+    if (ms > 65535) return PA_ERR_SHAPE;
+    const size_t need = pa_decode_workspace_bytes(batch, num_heads, num_kv_heads, head_dim, max_blocks_per_seq,
+                                                  block_size, split);
+    if (workspace_bytes < need) return PA_ERR_WORKSPACE;
+    if (need > 0 && (!workspace || !aligned(workspace, 16))) return PA_ERR_NULL;
+    pa::launch_decode_mfma(q, q_tok_stride, k_cache, v_cache, context_lens, block_table, max_blocks_per_seq, batch,
+                           num_heads, num_kv_heads, block_size, softmax_scale, out, out_bf16, split, ms, workspace,
+                           st);
+  } else {
+    pa::launch_attn_generic(dtype == PA_BF16, q, q_tok_stride, k_cache, v_cache, nullptr, nullptr, context_lens,
+                            block_table, max_blocks_per_seq, batch, batch, num_heads, num_kv_heads, head_dim,
+                            block_size, softmax_scale, out, out_bf16, st);
+  }
+  return launched();
+}
+
+}  // extern "C"

@@ -1,0 +1,32 @@
+// Internal launchers behind the C ABI (pa_api.hip validates every argument before calling these).
+#pragma once
+
+#include "pa_common.h"
+
+namespace pa {
+
+void launch_build_metadata(const int32_t* num_cached, const int32_t* num_new, const int32_t* block_table,
+                           int32_t mbps, int32_t batch, int32_t total_q, int32_t block_size, int32_t* cu_q,
+                           int32_t* cu_k, int32_t* ctx, int32_t* pos, int32_t* slot, hipStream_t stream);
+
+void launch_store_kvcache(const void* k, int64_t k_stride_bytes, const void* v, int64_t v_stride_bytes,
+                          void* k_cache, void* v_cache, const int32_t* slot_mapping, int32_t num_tokens,
+                          int64_t row_bytes, int vec_bytes, hipStream_t stream);
+
+void launch_attn_generic(bool bf16, const void* q, int64_t q_stride, const void* k_cache, const void* v_cache,
+                         const int32_t* cu_q, const int32_t* cu_k, const int32_t* ctx_lens,
+                         const int32_t* block_table, int32_t mbps, int32_t batch, int32_t rows, int32_t Hq,
+                         int32_t Hkv, int32_t D, int32_t block_size, float scale, void* out, bool out_bf16,
+                         hipStream_t stream);
+
+void launch_decode_mfma(const void* q, int64_t q_stride, const void* k_cache, const void* v_cache,
+                        const int32_t* ctx_lens, const int32_t* block_table, int32_t mbps, int32_t batch,
+                        int32_t Hq, int32_t Hkv, int32_t block_size, float scale, void* out, bool out_bf16,
+                        int32_t split_tokens, int32_t max_splits, void* workspace, hipStream_t stream);
+
+void launch_prefill_mfma(const void* q, int64_t q_stride, const void* k_cache, const void* v_cache,
+                         const int32_t* cu_q, const int32_t* cu_k, const int32_t* block_table, int32_t mbps,
+                         int32_t batch, int32_t max_seqlen_q, int32_t Hq, int32_t Hkv, int32_t block_size,
+                         float scale, void* out, bool out_bf16, hipStream_t stream);
+
+}  // namespace pa

@@ -1,0 +1,157 @@
+// Metadata build and store_kvcache kernels.
+//
+// Metadata: the flattening of a step's sequences into per-token positions and slots, and the prefix sums that
+// delimit sequences ("一个 prompt 的一生" §3.3.2, prepare_prefill example; slot formula of "Nano-vLLM 架构详解"
+// §1, Step2). Store: a bit copy of each new token's K/V row to its slot ("Nano-vLLM 架构详解" §3.2, KV cache
+// 写入函数).
+#include "pa_launch.h"
+
+namespace pa {
+
+// ------------------------------------------------------------------------------------------------- metadata
+//
+// Every workgroup rebuilds the two prefix sums over the batch in LDS (batch <= 8192, a few hundred adds per
+// thread at most), then handles 256 tokens: a binary search for the token's sequence, its absolute position
+// and its slot. Workgroup 0 also writes cu_seqlens_q/k and context_lens.
+constexpr int kMetaThreads = 256;
+
+__global__ __launch_bounds__(kMetaThreads) void build_metadata_kernel(
+    const int32_t* __restrict__ num_cached, const int32_t* __restrict__ num_new,
+    const int32_t* __restrict__ block_table, int32_t mbps, int32_t batch, int32_t total_q, int32_t block_size,
+    int32_t* __restrict__ cu_q_out, int32_t* __restrict__ cu_k_out, int32_t* __restrict__ ctx_out,
+    int32_t* __restrict__ pos_out, int32_t* __restrict__ slot_out) {
+  extern __shared__ int32_t smem[];
+  int32_t* cu_q = smem;                  // [batch + 1]
+  int32_t* cu_k = smem + (batch + 1);    // [batch + 1]
+  __shared__ int32_t part_q[kMetaThreads], part_k[kMetaThreads];
+
+  const int tid = threadIdx.x;
+  const int chunk = (batch + kMetaThreads - 1) / kMetaThreads;
+  const int lo = min(batch, tid * chunk), hi = min(batch, lo + chunk);
+  int32_t sq = 0, sk = 0;
+  for (int s = lo; s < hi; ++s) {
+    const int32_t n = num_new[s];
+    sq += n;
+    sk += num_cached[s] + n;
+  }
+  part_q[tid] = sq;
+  part_k[tid] = sk;
+  __syncthreads();
+  if (tid == 0) {  // exclusive scan of the 256 per-thread sums
+    int32_t aq = 0, ak = 0;
+    for (int t = 0; t < kMetaThreads; ++t) {
+      const int32_t q = part_q[t], k = part_k[t];
+      part_q[t] = aq;
+      part_k[t] = ak;
+      aq += q;
+      ak += k;
+    }
+    cu_q[0] = 0;
+    cu_k[0] = 0;
+  }
+  __syncthreads();
+  sq = part_q[tid];
+  sk = part_k[tid];
+  for (int s = lo; s < hi; ++s) {
+    const int32_t n = num_new[s];
+    const int32_t kl = num_cached[s] + n;
+    sq += n;
+    sk += kl;
+    cu_q[s + 1] = sq;
+    cu_k[s + 1] = sk;
+    if (blockIdx.x == 0) ctx_out[s] = kl;
+  }
+  __syncthreads();
+  if (blockIdx.x == 0) {
+    for (int s = tid; s <= batch; s += kMetaThreads) {
+      cu_q_out[s] = cu_q[s];
+      cu_k_out[s] = cu_k[s];
+    }
+  }
+  const int t = blockIdx.x * kMetaThreads + tid;
+  if (t >= total_q) return;
+  // largest s with cu_q[s] <= t (sequences with no new tokens have cu_q[s] == cu_q[s+1] and are skipped)
+  int a = 0, b = batch;  // invariant: cu_q[a] <= t < cu_q[b]
+  while (b - a > 1) {
+    const int mid = (a + b) >> 1;
+    if (cu_q[mid] <= t) a = mid; else b = mid;
+  }
+  const int32_t pos = num_cached[a] + (t - cu_q[a]);
+  const int32_t blk = pos / block_size;
+  const int32_t phys = block_table[int64_t(a) * mbps + blk];
+  pos_out[t] = pos;
+  slot_out[t] = phys * block_size + (pos - blk * block_size);
+}
+
+void launch_build_metadata(const int32_t* num_cached, const int32_t* num_new, const int32_t* block_table,
+                           int32_t mbps, int32_t batch, int32_t total_q, int32_t block_size, int32_t* cu_q,
+                           int32_t* cu_k, int32_t* ctx, int32_t* pos, int32_t* slot, hipStream_t stream) {
+  const int grid = total_q > 0 ? (total_q + kMetaThreads - 1) / kMetaThreads : 1;
+  const size_t lds = size_t(2) * (batch + 1) * sizeof(int32_t);
+  hipLaunchKernelGGL(build_metadata_kernel, dim3(grid), dim3(kMetaThreads), lds, stream, num_cached, num_new,
+                     block_table, mbps, batch, total_q, block_size, cu_q, cu_k, ctx, pos, slot);
+}
+
+// ------------------------------------------------------------------------------------------------- store
+//
+// One wave per token, four tokens per workgroup. A wave copies the token's K row then its V row
+// (num_kv_heads * head_dim elements each) with VEC-byte accesses; lanes cover consecutive VEC-byte pieces, so
+// each row is read and written as whole contiguous runs.
+constexpr int kStoreThreads = 256;
+
+template <typename VecT>
+__global__ __launch_bounds__(kStoreThreads) void store_kvcache_kernel(
+    const char* __restrict__ k, int64_t k_stride_bytes, const char* __restrict__ v, int64_t v_stride_bytes,
+    char* __restrict__ k_cache, char* __restrict__ v_cache, const int32_t* __restrict__ slot_mapping,
+    int32_t num_tokens, int32_t row_vecs) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * (kStoreThreads / 64) + (threadIdx.x >> 6);
+  if (t >= num_tokens) return;
+  const int32_t slot = slot_mapping[t];
+  if (slot < 0) return;
+  const int64_t row_bytes = int64_t(row_vecs) * sizeof(VecT);
+  const VecT* ks = reinterpret_cast<const VecT*>(k + t * k_stride_bytes);
+  const VecT* vs = reinterpret_cast<const VecT*>(v + t * v_stride_bytes);
+  VecT* kd = reinterpret_cast<VecT*>(k_cache + int64_t(slot) * row_bytes);
+  VecT* vd = reinterpret_cast<VecT*>(v_cache + int64_t(slot) * row_bytes);
+  for (int i = lane; i < row_vecs; i += 64) {
+    const VecT a = ks[i];
+    const VecT b = vs[i];
+    kd[i] = a;
+    vd[i] = b;
+  }
+}
+
+void launch_store_kvcache(const void* k, int64_t k_stride_bytes, const void* v, int64_t v_stride_bytes,
+                          void* k_cache, void* v_cache, const int32_t* slot_mapping, int32_t num_tokens,
+                          int64_t row_bytes, int vec_bytes, hipStream_t stream) {
+  const int grid = (num_tokens + kStoreThreads / 64 - 1) / (kStoreThreads / 64);
+  const char* kp = static_cast<const char*>(k);
+  const char* vp = static_cast<const char*>(v);
+  char* kc = static_cast<char*>(k_cache);
+  char* vc = static_cast<char*>(v_cache);
+  switch (vec_bytes) {
+    case 16:
+      hipLaunchKernelGGL(store_kvcache_kernel<u32x4>, dim3(grid), dim3(kStoreThreads), 0, stream, kp,
+                         k_stride_bytes, vp, v_stride_bytes, kc, vc, slot_mapping, num_tokens,
+                         int32_t(row_bytes / 16));
+      break;
+    case 8:
+      hipLaunchKernelGGL(store_kvcache_kernel<u32x2>, dim3(grid), dim3(kStoreThreads), 0, stream, kp,
+                         k_stride_bytes, vp, v_stride_bytes, kc, vc, slot_mapping, num_tokens,
+                         int32_t(row_bytes / 8));
+      break;
+    case 4:
+      hipLaunchKernelGGL(store_kvcache_kernel<uint32_t>, dim3(grid), dim3(kStoreThreads), 0, stream, kp,
+                         k_stride_bytes, vp, v_stride_bytes, kc, vc, slot_mapping, num_tokens,
+                         int32_t(row_bytes / 4));
+      break;
+    default:
+      hipLaunchKernelGGL(store_kvcache_kernel<uint16_t>, dim3(grid), dim3(kStoreThreads), 0, stream, kp,
+                         k_stride_bytes, vp, v_stride_bytes, kc, vc, slot_mapping, num_tokens,
+                         int32_t(row_bytes / 2));
+      break;
+  }
+}
+
+}  // namespace pa

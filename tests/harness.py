@@ -1,0 +1,117 @@
+"""Shared helpers of the GPU parity tests: upload seeded inputs, run the HIP path through the C ABI, compare with
+the oracle. Nothing here computes the method: the HIP side is paged_kv_cache_111_amd, the reference is oracle/.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import oracle
+import paged_kv_cache_111_amd as pa
+
+# Attention tolerance against the float64 oracle, over the whole output tensor of one call (bf16 inputs,
+# float32 accumulation and output).
+MAX_ABS = 2e-2
+REL_RMS = 5e-3
+
+DEV = "cuda:0"
+
+
+def to_dev(arr: np.ndarray, dtype: str) -> torch.Tensor:
+    if dtype == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(arr).view(np.int16)).view(torch.bfloat16).to(DEV)
+    return torch.from_numpy(np.ascontiguousarray(arr, dtype=np.float32)).to(DEV)
+
+
+def to_host_bits(t: torch.Tensor) -> np.ndarray:
+    """Raw stored values on the host: uint16 bf16 bits or float32."""
+    t = t.detach().cpu().contiguous()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    return t.numpy()
+
+
+def i32(a) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(DEV)
+
+
+class DevStep:
+    """One step's inputs on the device."""
+
+    def __init__(self, step, dtype: str):
+        self.step = step
+        self.block_table = i32(step.block_table)
+        self.num_cached = i32(step.num_cached)
+        self.num_new = i32(step.num_new)
+        self.q = to_dev(step.q, dtype)
+        self.k = to_dev(step.k, dtype)
+        self.v = to_dev(step.v, dtype)
+        self.total_q = int(step.num_new.sum())
+        self.max_q = int(step.num_new.max()) if step.batch else 0
+        self.max_k = int((step.num_cached + step.num_new).max()) if step.batch else 0
+
+
+def hip_step(wl, ds: DevStep, kc: torch.Tensor, vc: torch.Tensor, out_dtype=torch.float32, split_tokens=0):
+    """The whole path on the GPU: metadata, store, attention. Returns (metadata tensors, output tensor)."""
+    meta = pa.build_metadata(ds.num_cached, ds.num_new, ds.block_table, ds.total_q, wl.num_blocks, wl.block_size)
+    pa.store_kvcache(ds.k, ds.v, kc, vc, meta["slot_mapping"])
+    if ds.step.kind == "prefill":
+        out = pa.prefill_varlen(ds.q, kc, vc, meta["cu_seqlens_q"], meta["cu_seqlens_k"], ds.block_table, ds.max_q,
+                                ds.max_k, wl.scale, out_dtype=out_dtype)
+    else:
+        out = pa.decode(ds.q, kc, vc, meta["context_lens"], ds.block_table, wl.scale, out_dtype=out_dtype,
+                        split_tokens=split_tokens)
+    return meta, out
+
+
+def compare_metadata(meta_dev: dict, meta_ref: dict) -> None:
+    for key in ("cu_seqlens_q", "cu_seqlens_k", "context_lens", "positions", "slot_mapping"):
+        got = meta_dev[key].cpu().numpy()
+        assert np.array_equal(got, meta_ref[key]), f"{key} differs"
+
+
+def attention_errors(out: torch.Tensor, ref: np.ndarray, rows=None):
+    """(max_abs, rel_rms) over the rows the oracle computed (all rows by default)."""
+    got = out.detach().float().cpu().numpy().astype(np.float64)
+    if rows is not None:
+        got, ref = got[rows], ref[rows]
+    assert np.all(np.isfinite(ref))
+    assert np.all(np.isfinite(got)), "non-finite output"
+    err = got - ref
+    max_abs = float(np.max(np.abs(err)))
+    rel_rms = float(np.sqrt(np.sum(err * err) / np.sum(ref * ref)))
+    return max_abs, rel_rms
+
+
+def assert_close(out: torch.Tensor, ref: np.ndarray, rows=None, what: str = "") -> tuple:
+    max_abs, rel_rms = attention_errors(out, ref, rows)
+    if out.dtype == torch.bfloat16:
+        # the output rounding adds up to half a bf16 ulp of |O|
+        got = out.detach().float().cpu().numpy().astype(np.float64)
+        r = ref if rows is None else ref[rows]
+        g = got if rows is None else got[rows]
+        ulp = np.exp2(np.floor(np.log2(np.maximum(np.abs(r), 1e-30))) - 7)
+        assert np.all(np.abs(g - r) <= MAX_ABS + 0.5 * ulp), f"{what}: bf16 output off by more than tol + ulp/2"
+        assert rel_rms <= REL_RMS + 4e-3, f"{what}: rel_rms {rel_rms:.3g}"
+    else:
+        assert max_abs <= MAX_ABS, f"{what}: max_abs {max_abs:.3g} > {MAX_ABS}"
+        assert rel_rms <= REL_RMS, f"{what}: rel_rms {rel_rms:.3g} > {REL_RMS}"
+    return max_abs, rel_rms
+
+
+def oracle_step(wl, step, kc_host: np.ndarray, vc_host: np.ndarray, seqs=None, rows=None):
+    """Oracle metadata, store (in place on the host pools) and attention for one step."""
+    return oracle.run_step(step, kc_host, vc_host, wl.block_size, wl.scale, wl.dtype, seqs=seqs, rows=rows)
+
+
+def flat_rows(meta_ref: dict, seqs, rows_by_seq=None):
+    """Flattened output rows covered by the given sequences (and row subsets)."""
+    cu = meta_ref["cu_seqlens_q"]
+    out = []
+    for s in seqs:
+        if rows_by_seq is not None and s in rows_by_seq:
+            out.extend(int(cu[s]) + np.asarray(rows_by_seq[s]))
+        else:
+            out.extend(range(int(cu[s]), int(cu[s + 1])))
+    return np.asarray(out, dtype=np.int64)

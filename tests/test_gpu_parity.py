@@ -1,0 +1,284 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle, on the same seeded inputs.
+
+Bit-exact for metadata (slots, prefix sums, lengths) and for the cache after store_kvcache; attention within
+max-abs 2e-2 and relative RMS 5e-3 of the float64 oracle (bf16 inputs, float32 accumulation and output).
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_kv_cache_111_amd as pa
+from harness import DEV, DevStep, assert_close, compare_metadata, flat_rows, hip_step, i32, oracle_step, to_dev, \
+    to_host_bits
+from workloads import build_decode, build_prefill, make_config
+
+pytestmark = pytest.mark.gpu
+
+
+def _run_and_check(wl, out_dtype=torch.float32, split_tokens=0, seqs=None, rows=None, check_pool=True):
+    """Every step of the workload on both sides; returns the per-step (max_abs, rel_rms)."""
+    kc_h, vc_h = wl.k_cache.copy(), wl.v_cache.copy()
+    kc, vc = to_dev(wl.k_cache, wl.dtype), to_dev(wl.v_cache, wl.dtype)
+    errs = []
+    for i, step in enumerate(wl.steps):
+        print(f"[case] {wl.name} step {i} {step.kind} B={step.batch} T={step.num_tokens}", flush=True)
+        ds = DevStep(step, wl.dtype)
+        meta_d, out = hip_step(wl, ds, kc, vc, out_dtype=out_dtype, split_tokens=split_tokens)
+        torch.cuda.synchronize()
+        meta_r, ref = oracle_step(wl, step, kc_h, vc_h, seqs=seqs, rows=rows)
+        compare_metadata(meta_d, meta_r)
+        if check_pool:
+            assert np.array_equal(to_host_bits(kc), kc_h), "K cache differs after store"
+            assert np.array_equal(to_host_bits(vc), vc_h), "V cache differs after store"
+        frows = None if seqs is None else flat_rows(meta_r, seqs, rows)
+        errs.append(assert_close(out, ref, frows, what=f"{wl.name} step {i}"))
+    return errs
+
+
+# ------------------------------------------------------------------------------------------------ named configs
+
+
+def test_tiny_config():
+    _run_and_check(make_config("tiny"))
+
+
+def test_decode_qwen3_0p6b_config():
+    _run_and_check(make_config("decode_qwen3_0p6b"))
+
+
+def test_prefill_qwen3_8b_config():
+    _run_and_check(make_config("prefill_qwen3_8b"))
+
+
+def test_chunked_qwen3_8b_config_sampled_rows():
+    wl = make_config("chunked_qwen3_8b")
+    rows = {0: np.concatenate([np.arange(0, 64), np.arange(1000, 1064), np.arange(1984, 2048)])}
+    _run_and_check(wl, seqs=[0], rows=rows)
+
+
+@pytest.fixture(scope="module")
+def decode_32b():
+    return make_config("decode_qwen3_32b")
+
+
+def test_decode_qwen3_32b_config_sampled(decode_32b):
+    """Full-size pool (offsets beyond 2^31 elements); the oracle checks 16 sequences, the store every slot."""
+    wl = decode_32b
+    step = wl.steps[0]
+    ctx = step.num_cached + 1
+    shared = wl.notes["shared"]
+    pick = {int(np.argmax(ctx)), int(np.argmin(ctx)), shared[0][0], shared[0][1], shared[1][0], shared[1][1]}
+    rng = np.random.default_rng(7)
+    pick |= set(rng.choice(step.batch, 10, replace=False).tolist())
+    seqs = sorted(pick)
+    print(f"[case] decode_qwen3_32b seqs {seqs}", flush=True)
+    kc, vc = to_dev(wl.k_cache, wl.dtype), to_dev(wl.v_cache, wl.dtype)
+    kc0 = kc.clone()
+    ds = DevStep(step, wl.dtype)
+    meta_d, out = hip_step(wl, ds, kc, vc)
+    torch.cuda.synchronize()
+    meta_r, ref = oracle_step(wl, step, wl.k_cache, wl.v_cache, seqs=seqs)  # idempotent store into the fixture
+    compare_metadata(meta_d, meta_r)
+    # store: the written rows hold the new keys; every other row is unchanged
+    row = wl.num_kv_heads * wl.head_dim
+    changed = torch.nonzero((kc.view(-1, row) != kc0.view(-1, row)).any(dim=1)).flatten().cpu().numpy()
+    slots = meta_r["slot_mapping"]
+    assert set(changed.tolist()) <= set(slots.tolist())
+    got_rows = to_host_bits(kc.view(-1, row)[torch.from_numpy(slots.astype(np.int64)).to(DEV)])
+    assert np.array_equal(got_rows, step.k.reshape(step.batch, row))
+    del kc0
+    assert_close(out, ref, flat_rows(meta_r, seqs), what="decode_qwen3_32b")
+
+
+@pytest.mark.parametrize("split", [32, 256, 4096, 32768])
+def test_decode_qwen3_32b_split_sizes(decode_32b, split):
+    """Split-K with many, few and a single split per sequence gives the same answer within tolerance."""
+    wl = decode_32b
+    step = wl.steps[0]
+    seqs = [0, 1, 2, 3, int(np.argmax(step.num_cached))]
+    kc, vc = to_dev(wl.k_cache, wl.dtype), to_dev(wl.v_cache, wl.dtype)
+    ds = DevStep(step, wl.dtype)
+    print(f"[case] decode_qwen3_32b split {split}", flush=True)
+    _, out = hip_step(wl, ds, kc, vc, split_tokens=split)
+    torch.cuda.synchronize()
+    meta_r, ref = oracle_step(wl, step, wl.k_cache, wl.v_cache, seqs=seqs)
+    assert_close(out, ref, flat_rows(meta_r, seqs), what=f"split {split}")
+
+
+# ------------------------------------------------------------------------------------------------ small shapes
+
+PREFILL_CASES = [
+    # Hq, Hkv, D, bs, dtype, k_lens, cached
+    (32, 8, 128, 256, "bf16", [300, 129, 1000, 17], [256, 0, 512, 0]),
+    (8, 8, 128, 16, "bf16", [77, 200, 33, 1], [10, 150, 0, 0]),
+    (16, 1, 128, 32, "bf16", [260, 5, 64], [3, 0, 63]),
+    (12, 4, 128, 24, "bf16", [100, 61, 130], [50, 0, 129]),
+    (4, 2, 64, 16, "bf16", [40, 17], [8, 0]),
+    (8, 2, 128, 16, "f32", [70, 33], [20, 0]),
+    (4, 4, 16, 4, "f32", [9, 13], [0, 5]),
+    (32, 8, 128, 256, "bf16", [2048], [0]),
+]
+
+
+@pytest.mark.parametrize("case", range(len(PREFILL_CASES)))
+def test_prefill_small(case):
+    Hq, Hkv, D, bs, dt, kl, cached = PREFILL_CASES[case]
+    wl = build_prefill(f"prefill_small_{case}", 200 + case, Hq, Hkv, D, bs, dt, kl, cached,
+                       num_blocks=sum(-(-n // bs) for n in kl) + 3)
+    _run_and_check(wl)
+
+
+DECODE_CASES = [
+    # Hq, Hkv, D, bs, dtype, ctx, split
+    (16, 8, 128, 256, "bf16", [1, 255, 256, 257, 4096, 1000], 0),
+    (16, 8, 128, 256, "bf16", [1, 255, 256, 257, 4096, 1000], 32),
+    (64, 8, 128, 256, "bf16", [33, 700, 2049], 256),
+    (16, 1, 128, 16, "bf16", [50, 17, 300], 64),
+    (8, 2, 128, 24, "bf16", [100, 49, 1], 96),
+    (32, 1, 128, 16, "bf16", [40, 90], 0),
+    (8, 2, 128, 16, "f32", [70, 33], 0),
+    (4, 2, 64, 16, "bf16", [70, 33], 0),
+]
+
+
+@pytest.mark.parametrize("case", range(len(DECODE_CASES)))
+def test_decode_small(case):
+    Hq, Hkv, D, bs, dt, ctx, split = DECODE_CASES[case]
+    wl = build_decode(f"decode_small_{case}", 300 + case, Hq, Hkv, D, bs, dt, ctx,
+                      num_blocks=sum(-(-n // bs) for n in ctx) + 2)
+    _run_and_check(wl, split_tokens=split)
+
+
+def test_bf16_output():
+    wl = build_prefill("bf16_out", 400, 32, 8, 128, 256, "bf16", [300, 700], [256, 0])
+    _run_and_check(wl, out_dtype=torch.bfloat16)
+    wl = build_decode("bf16_out_d", 401, 16, 8, 128, 256, "bf16", [300, 3000])
+    _run_and_check(wl, out_dtype=torch.bfloat16, split_tokens=256)
+
+
+# ------------------------------------------------------------------------------------------------ properties
+
+
+def _relabel(wl, perm):
+    kc = np.empty_like(wl.k_cache)
+    vc = np.empty_like(wl.v_cache)
+    kc[perm] = wl.k_cache
+    vc[perm] = wl.v_cache
+    st = wl.steps[0]
+    bt = np.where(st.block_table >= 0, perm[np.maximum(st.block_table, 0)], -1).astype(np.int32)
+    return kc, vc, type(st)(st.kind, bt, st.num_cached, st.num_new, st.q, st.k, st.v)
+
+
+@pytest.mark.parametrize("kind", ["prefill", "decode"])
+def test_physical_relabelling_is_bit_identical(kind):
+    if kind == "prefill":
+        wl = build_prefill("perm_p", 500, 32, 8, 128, 64, "bf16", [300, 129, 500], [64, 0, 128], num_blocks=20)
+    else:
+        wl = build_decode("perm_d", 501, 64, 8, 128, 64, "bf16", [300, 129, 1500], num_blocks=40)
+    perm = np.random.default_rng(3).permutation(wl.num_blocks)
+    kc2, vc2, st2 = _relabel(wl, perm)
+    outs = []
+    for kch, vch, st in ((wl.k_cache, wl.v_cache, wl.steps[0]), (kc2, vc2, st2)):
+        kc, vc = to_dev(kch, wl.dtype), to_dev(vch, wl.dtype)
+        _, out = hip_step(wl, DevStep(st, wl.dtype), kc, vc, split_tokens=128)
+        outs.append(out.cpu())
+    assert torch.equal(outs[0], outs[1])
+
+
+@pytest.mark.parametrize("kind", ["prefill", "decode"])
+def test_nan_in_unreferenced_slots_does_not_reach_output(kind):
+    if kind == "prefill":
+        wl = build_prefill("nan_p", 510, 32, 8, 128, 256, "bf16", [300, 77], [256, 0], num_blocks=6)
+    else:
+        wl = build_decode("nan_d", 511, 16, 8, 128, 256, "bf16", [300, 77, 513], num_blocks=8)
+    st = wl.steps[0]
+    k_len = st.num_cached + st.num_new
+    keep = np.zeros(wl.num_blocks * wl.block_size, bool)
+    for s in range(st.batch):
+        ids = st.block_table[s][:oracle.num_blocks(int(k_len[s]), wl.block_size)]
+        keep[oracle.get_slots(ids, wl.block_size, int(k_len[s]))] = True
+    outs = []
+    for poison in (False, True):
+        kch, vch = wl.k_cache.copy(), wl.v_cache.copy()
+        if poison:
+            kch.reshape(-1, wl.num_kv_heads, wl.head_dim)[~keep] = 0x7FC0  # bf16 quiet NaN
+            vch.reshape(-1, wl.num_kv_heads, wl.head_dim)[~keep] = 0x7FC0
+        kc, vc = to_dev(kch, wl.dtype), to_dev(vch, wl.dtype)
+        _, out = hip_step(wl, DevStep(st, wl.dtype), kc, vc, split_tokens=64)
+        outs.append(out.cpu())
+    assert torch.isfinite(outs[1]).all()
+    assert torch.equal(outs[0], outs[1])
+
+
+def test_store_slot_102_changes_exactly_one_row():
+    """The worked slot example on the device: one token stored at slot 25*4+2 of a bs=4 pool."""
+    nb, bs, Hkv, D = 32, 4, 2, 16
+    rng = np.random.default_rng(9)
+    kc_h = rng.standard_normal((nb, bs, Hkv, D)).astype(np.float32)
+    kc, vc = to_dev(kc_h, "f32"), to_dev(kc_h, "f32")
+    k = torch.from_numpy(rng.standard_normal((3, Hkv, D)).astype(np.float32)).to(DEV)
+    pa.store_kvcache(k, k, kc, vc, i32([-1, oracle.slot_of(25, 4, 2), -1]))
+    got = to_host_bits(kc)
+    diff = np.flatnonzero((got != kc_h).reshape(-1))
+    row = Hkv * D
+    assert diff.min() >= 102 * row and diff.max() < 103 * row
+    assert np.array_equal(got[25, 2], k[1].cpu().numpy())
+
+
+def test_store_from_strided_fused_qkv():
+    """k and v as views of a fused [T, (Hq + 2 Hkv) * D] projection output (token stride > row)."""
+    Hq, Hkv, D, bs, nb, T = 32, 8, 128, 256, 8, 300
+    rng = np.random.default_rng(10)
+    qkv = torch.from_numpy(rng.standard_normal((T, (Hq + 2 * Hkv) * D)).astype(np.float32)).to(DEV).bfloat16()
+    k = qkv[:, Hq * D:(Hq + Hkv) * D].view(T, Hkv, D)
+    v = qkv[:, (Hq + Hkv) * D:].view(T, Hkv, D)
+    kc = torch.zeros((nb, bs, Hkv, D), dtype=torch.bfloat16, device=DEV)
+    vc = torch.zeros_like(kc)
+    slots = rng.permutation(nb * bs)[:T].astype(np.int32)
+    pa.store_kvcache(k, v, kc, vc, i32(slots))
+    kh, vh = to_host_bits(kc).reshape(nb * bs, -1), to_host_bits(vc).reshape(nb * bs, -1)
+    ref_k = np.zeros_like(kh)
+    ref_v = np.zeros_like(vh)
+    oracle.store_kvcache(ref_k.reshape(nb, bs, Hkv, D), ref_v.reshape(nb, bs, Hkv, D),
+                         to_host_bits(k.contiguous()), to_host_bits(v.contiguous()), slots)
+    assert np.array_equal(kh, ref_k) and np.array_equal(vh, ref_v)
+
+
+def test_metadata_prepare_prefill_example(golden):
+    g = golden["prepare_prefill"]
+    table = i32([[7], [3]])
+    meta = pa.build_metadata(i32([0, 0]), i32([3, 2]), table, 5, 16, g["block_size"])
+    assert meta["positions"].cpu().tolist() == g["positions"]
+    assert meta["cu_seqlens_q"].cpu().tolist() == g["cu_seqlens_q"]
+    assert meta["slot_mapping"].cpu().tolist() == g["slot_mapping"]
+
+
+def test_metadata_chunked_counters_example(golden):
+    g = golden["chunked_counters"]
+    table = i32([g["block_table"]])
+    full = oracle.get_slots(g["block_table"], g["block_size"], g["prompt"])
+    for ch in g["chunks"]:
+        meta = pa.build_metadata(i32([ch["num_cached"]]), i32([ch["num_scheduled"]]), table, ch["num_scheduled"],
+                                 16, g["block_size"])
+        assert meta["context_lens"].cpu().tolist() == [ch["cached_after"]]
+        assert meta["slot_mapping"].cpu().tolist() == full[ch["num_cached"]:ch["cached_after"]]
+
+
+def test_metadata_large_batch_bit_exact():
+    rng = np.random.default_rng(11)
+    B, bs = 3000, 16
+    cached = rng.integers(0, 200, B)
+    new = rng.integers(0, 40, B)
+    nbk = [-(-(int(c) + int(n)) // bs) for c, n in zip(cached, new)]
+    perm = rng.permutation(sum(nbk) + 5).astype(np.int32)
+    width = max(nbk)
+    table = np.full((B, width), -1, np.int32)
+    at = 0
+    for s in range(B):
+        table[s, :nbk[s]] = perm[at:at + nbk[s]]
+        at += nbk[s]
+    ref = oracle.build_metadata(table, cached, new, bs)
+    meta = pa.build_metadata(i32(cached), i32(new), i32(table), int(new.sum()), len(perm), bs)
+    compare_metadata(meta, ref)
