@@ -1,0 +1,348 @@
+"""Benchmark of the paged-KV attention step on one MI355X.
+
+One step = one pass of the whole path over one batch: device-side metadata (slots, prefix sums), store_kvcache
+of the new tokens, then attention over the paged cache (decode: split pass + merge pass; prefill: one pass).
+
+Main line: the decode workload with Qwen3-0.6B attention shape (64 sequences, 16 query / 8 KV heads, head_dim
+128, bf16, block_size 256, contexts U[128, 4096]). Consecutive steps use different per-layer cache pools (the
+same block tables, as in an engine whose pool is [2, num_layers, num_blocks, block_size, Hkv, D]), so the KV a
+step reads was not touched by the previous few steps and cannot sit in the 256 MB last-level cache.
+
+Printed: one JSON line with the whole-step throughput (`value`, GB/s of algorithmic bytes), the roofline of
+the decode attention call measured with HIP events on the launch stream, the oracle's CPU throughput on a
+bounded sample, and secondary entries for the prefill and long-context decode workloads.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, GB/s
+MFMA_BF16_PEAK_TFLOPS = 2516.6  # MI355X dense bf16 MFMA, TFLOP/s (256 CU x 2.4 GHz x 4096 flop/clk)
+METRIC = "decode paged-attn KV GB/s (% HBM peak); prefill attn TFLOP/s (% MFMA peak)"
+
+
+# ---------------------------------------------------------------------------------------------- workload sizes
+
+
+def algorithmic_work(wl, step, out_bytes: int):
+    """Bytes (decode, store, metadata) and flops (prefill) the method must move or compute for one step.
+
+    Decode: each needed KV row once (2 * Hkv * D * elem bytes per token), Q, O, the used block-table entries and
+    the context lengths; shared prefix blocks of one call are counted once. Store: the new K/V rows read and
+    written plus slot_mapping. Prefill flops: 4 * D * Hq per unmasked (query, key) pair.
+    """
+    E = wl.elem_bytes
+    kv_tok = 2 * wl.num_kv_heads * wl.head_dim * E
+    B = step.batch
+    k_len = (step.num_cached + step.num_new).astype(np.int64)
+    q_len = step.num_new.astype(np.int64)
+    T = int(q_len.sum())
+    shared = wl.notes.get("shared", [])
+    shared_tokens = sum(n * wl.block_size for _, _, n in shared)
+    n_tbl = int(sum(-(-int(n) // wl.block_size) for n in k_len))
+    kv_bytes = (int(k_len.sum()) - shared_tokens) * kv_tok
+    q_bytes = T * wl.num_heads * wl.head_dim * E
+    o_bytes = T * wl.num_heads * wl.head_dim * out_bytes
+    attn_bytes = kv_bytes + q_bytes + o_bytes + 4 * n_tbl + 4 * B
+    store_bytes = 2 * T * kv_tok + 4 * T
+    meta_bytes = 4 * (3 * B + n_tbl) + 4 * (3 * B + 2 + 2 * T)
+    past = k_len - q_len
+    pairs = int(np.sum(q_len * past + q_len * (q_len + 1) // 2))
+    flops = 4 * wl.head_dim * wl.num_heads * pairs
+    return {"kv_bytes": kv_bytes, "attn_bytes": attn_bytes, "store_bytes": store_bytes, "meta_bytes": meta_bytes,
+            "pairs": pairs, "flops": flops, "sum_k": int(k_len.sum()), "tokens": T}
+
+
+# ---------------------------------------------------------------------------------------------- GPU timing
+
+
+def _src_sha(*names) -> str:
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "paged_kv_cache_111_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def _traffic(profile_name: str, sha: str):
+    """HBM bytes per launch from a committed counter summary, or None if absent or taken on other sources."""
+    p = os.path.join(ROOT, "profiles", profile_name)
+    if not os.path.exists(p):
+        return None
+    with open(p, encoding="utf-8") as f:
+        d = json.load(f)
+    if d.get("source_sha") != sha:
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+class GpuWorkload:
+    """A workload's inputs on the device, with n_layers independent cache pools holding the same contents."""
+
+    def __init__(self, wl, n_layers: int, out_dtype):
+        import torch
+
+        self.torch = torch
+        self.wl = wl
+        self.step = wl.steps[-1]
+        dev = "cuda:0"
+
+        def up(a):
+            if wl.dtype == "bf16":
+                return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+            return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+        def i32(a):
+            return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(dev)
+
+        k0, v0 = up(wl.k_cache), up(wl.v_cache)
+        self.k_layers = [k0] + [k0.clone() for _ in range(n_layers - 1)]
+        self.v_layers = [v0] + [v0.clone() for _ in range(n_layers - 1)]
+        st = self.step
+        self.block_table = i32(st.block_table)
+        self.num_cached = i32(st.num_cached)
+        self.num_new = i32(st.num_new)
+        self.q, self.k, self.v = up(st.q), up(st.k), up(st.v)
+        self.total_q = int(st.num_new.sum())
+        self.max_q = int(st.num_new.max())
+        self.max_k = int((st.num_cached + st.num_new).max())
+        self.out = torch.empty((st.num_tokens, wl.num_heads, wl.head_dim), dtype=out_dtype, device=dev)
+        import paged_kv_cache_111_amd as pa
+
+        self.pa = pa
+        if st.kind == "decode":
+            need = pa.decode_workspace_bytes(st.batch, wl.num_heads, wl.num_kv_heads, wl.head_dim,
+                                             st.block_table.shape[1], wl.block_size, 0)
+        else:
+            need = pa.prefill_workspace_bytes(st.batch, wl.num_heads, wl.head_dim, self.max_q, self.max_k)
+        self.ws = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+
+    def run(self, layer: int, ev=None):
+        """One step on layer `layer`'s pool; ev = (e0, e1, e2, e3) events around metadata, store, attention."""
+        pa, wl, st = self.pa, self.wl, self.step
+        kc, vc = self.k_layers[layer], self.v_layers[layer]
+        if ev:
+            ev[0].record()
+        meta = pa.build_metadata(self.num_cached, self.num_new, self.block_table, self.total_q, wl.num_blocks,
+                                 wl.block_size)
+        if ev:
+            ev[1].record()
+        pa.store_kvcache(self.k, self.v, kc, vc, meta["slot_mapping"])
+        if ev:
+            ev[2].record()
+        if st.kind == "decode":
+            pa.decode(self.q, kc, vc, meta["context_lens"], self.block_table, wl.scale, out=self.out,
+                      workspace=self.ws)
+        else:
+            pa.prefill_varlen(self.q, kc, vc, meta["cu_seqlens_q"], meta["cu_seqlens_k"], self.block_table,
+                              self.max_q, self.max_k, wl.scale, out=self.out, workspace=self.ws)
+        if ev:
+            ev[3].record()
+
+
+def time_workload(g: GpuWorkload, steps: int, warmup: int, n_layers: int):
+    torch = g.torch
+    for i in range(warmup):
+        g.run(i % n_layers)
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        g.run(i % n_layers, evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    meta_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
+    store_ms = np.array([e[1].elapsed_time(e[2]) for e in evs])
+    attn_ms = np.array([e[2].elapsed_time(e[3]) for e in evs])
+    step_ms = np.array([e[0].elapsed_time(e[3]) for e in evs])
+    return {"wall_ms_per_step": 1e3 * wall / steps, "step_ms": float(np.mean(step_ms)),
+            "meta_ms": float(np.mean(meta_ms)), "store_ms": float(np.mean(store_ms)),
+            "attn_ms": float(np.mean(attn_ms)), "attn_ms_median": float(np.median(attn_ms)),
+            "attn_ms_min": float(np.min(attn_ms))}
+
+
+# ---------------------------------------------------------------------------------------------- CPU baseline
+
+
+def cpu_baseline(wl, budget_s: float):
+    """The oracle (as it stands) on the host: metadata, store and attention of the same step.
+
+    Whole passes over the batch are repeated until the time budget is spent; if one pass alone would exceed it,
+    the attention stops after the sequence that crosses the budget. The oracle's store writes the same rows on
+    every pass, so it runs in place on the workload's host pools.
+    """
+    import oracle
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        blas = max((d.get("num_threads", 1) for d in threadpool_info()), default=1)
+    except Exception:  # pragma: no cover - threadpoolctl missing
+        blas = 1
+    st = wl.steps[-1]
+    k_len = st.num_cached + st.num_new
+    secs, keys, pairs, seqs_done, passes = 0.0, 0, 0, 0, 0
+    while secs < budget_s:
+        t0 = time.perf_counter()
+        meta = oracle.build_metadata(st.block_table, st.num_cached, st.num_new, wl.block_size)
+        oracle.store_kvcache(wl.k_cache, wl.v_cache, st.k, st.v, meta["slot_mapping"])
+        secs += time.perf_counter() - t0
+        for s in range(st.batch):
+            t1 = time.perf_counter()
+            if st.kind == "decode":
+                oracle.decode(st.q, wl.k_cache, wl.v_cache, meta["context_lens"], st.block_table, wl.scale,
+                              wl.dtype, seqs=[s])
+            else:
+                oracle.prefill_varlen(st.q, wl.k_cache, wl.v_cache, meta["cu_seqlens_q"], meta["cu_seqlens_k"],
+                                      st.block_table, wl.scale, wl.dtype, seqs=[s])
+            secs += time.perf_counter() - t1
+            seqs_done += 1
+            keys += int(k_len[s])
+            ql = int(st.num_new[s])
+            pairs += ql * (int(k_len[s]) - ql) + ql * (ql + 1) // 2
+            if secs > budget_s:
+                break
+        passes += 1
+    kv_tok = 2 * wl.num_kv_heads * wl.head_dim * wl.elem_bytes
+    if st.kind == "decode":
+        value, unit = keys * kv_tok / secs / 1e9, "GB/s"
+    else:
+        value, unit = 4 * wl.head_dim * wl.num_heads * pairs / secs / 1e12, "TFLOP/s"
+    return {"value": round(value, 4), "unit": unit, "cores": int(blas), "kind": "oracle",
+            "host_cpus": len(os.sched_getaffinity(0)),
+            "sample": f"{passes} pass(es) of oracle metadata + store + float64 attention over the same step; "
+                      f"{seqs_done} sequence attentions ({keys} keys) in {secs:.1f} s; cores = BLAS threads"}
+
+
+# ---------------------------------------------------------------------------------------------- main
+
+
+def bench_one(name: str, steps: int, warmup: int, n_layers: int, out_dtype_name: str):
+    import torch
+
+    from workloads import make_config
+
+    wl = make_config(name)
+    out_dtype = torch.bfloat16 if out_dtype_name == "bf16" else torch.float32
+    g = GpuWorkload(wl, n_layers, out_dtype)
+    t = time_workload(g, steps, warmup, n_layers)
+    work = algorithmic_work(wl, g.step, 2 if out_dtype == torch.bfloat16 else 4)
+    res = {"workload": name, "kind": g.step.kind, "timing": t, "work": work}
+    if g.step.kind == "decode":
+        res["attn_GBps"] = work["attn_bytes"] / (t["attn_ms"] * 1e-3) / 1e9
+        res["attn_frac_hbm"] = res["attn_GBps"] / HBM_PEAK_GBS
+        res["step_GBps"] = (work["attn_bytes"] + work["store_bytes"] + work["meta_bytes"]) / (t["wall_ms_per_step"] * 1e-3) / 1e9
+    else:
+        res["attn_TFLOPs"] = work["flops"] / (t["attn_ms"] * 1e-3) / 1e12
+        res["attn_frac_mfma"] = res["attn_TFLOPs"] / MFMA_BF16_PEAK_TFLOPS
+        res["step_TFLOPs"] = work["flops"] / (t["wall_ms_per_step"] * 1e-3) / 1e12
+    res["store_GBps"] = work["store_bytes"] / (t["store_ms"] * 1e-3) / 1e9
+    del g
+    torch.cuda.empty_cache()
+    return wl, res
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--layers", type=int, default=8, help="cache pools cycled through by consecutive steps")
+    ap.add_argument("--out-dtype", default="bf16", choices=["bf16", "f32"])
+    ap.add_argument("--only", default=None, help="run one workload only (no secondary entries)")
+    ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for the CPU baseline")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run a plain 1 GiB copy kernel (reference for the HBM byte counters)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the attention step runs "
+              "on one GPU's share and has no cross-GPU exchange)", file=sys.stderr)
+        return 2
+    import torch
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    main_name = args.only or "decode_qwen3_0p6b"
+    wl, main = bench_one(main_name, args.steps, args.warmup, args.layers, args.out_dtype)
+    print(f"[bench] {main_name}: {json.dumps(main['timing'])}", file=sys.stderr, flush=True)
+    secondary = []
+    if not args.only and not args.no_secondary:
+        for name in ("prefill_qwen3_8b", "chunked_qwen3_8b", "decode_qwen3_32b"):
+            layers = 1 if name == "decode_qwen3_32b" else args.layers
+            _, r = bench_one(name, max(5, args.steps // 5), max(2, args.warmup // 2), layers, args.out_dtype)
+            print(f"[bench] {name}: {json.dumps(r['timing'])}", file=sys.stderr, flush=True)
+            entry = {"workload": name, "attn_ms": round(r["timing"]["attn_ms"], 4),
+                     "step_ms": round(r["timing"]["wall_ms_per_step"], 4),
+                     "store_GBps": round(r["store_GBps"], 1)}
+            if r["kind"] == "decode":
+                entry.update({"attn_GBps": round(r["attn_GBps"], 1), "frac_hbm": round(r["attn_frac_hbm"], 4),
+                              "kv_bytes": r["work"]["kv_bytes"]})
+            else:
+                entry.update({"attn_TFLOPs": round(r["attn_TFLOPs"], 1),
+                              "frac_mfma": round(r["attn_frac_mfma"], 4), "flops": r["work"]["flops"]})
+            secondary.append(entry)
+    if args.calibrate_copy:
+        x = torch.empty(1 << 29, dtype=torch.float16, device="cuda:0").normal_()
+        y = torch.empty_like(x)
+        for _ in range(3):
+            torch.mul(x, 1.0, out=y)  # reads 1 GiB, writes 1 GiB
+        torch.cuda.synchronize()
+        del x, y
+
+    t = main["timing"]
+    work = main["work"]
+    is_dec = main["kind"] == "decode"
+    sha = _src_sha("pa_decode.hip") if is_dec else _src_sha("pa_prefill.hip")
+    traffic = _traffic(f"{main_name}_hbm_traffic.json", sha)
+    if is_dec:
+        value = main["step_GBps"]
+        roof = {"bound": "hbm", "achieved": round(main["attn_GBps"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(main["attn_frac_hbm"], 4), "traffic": traffic,
+                "kernel": "pa_decode (decode_mfma_kernel + decode_reduce_kernel)",
+                "bytes_per_launch": work["attn_bytes"], "launch_ms": round(t["attn_ms"], 5)}
+        unit = "GB/s"
+    else:
+        value = work["flops"] / (t["wall_ms_per_step"] * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(main["attn_TFLOPs"], 1), "peak": MFMA_BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(main["attn_frac_mfma"], 4), "traffic": traffic,
+                "kernel": "prefill_mfma_kernel", "flops_per_launch": work["flops"],
+                "launch_ms": round(t["attn_ms"], 5)}
+        unit = "TFLOP/s"
+    st = wl.steps[-1]
+    line = {
+        "metric": METRIC, "value": round(value, 2), "unit": unit, "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(t["wall_ms_per_step"], 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": main_name, "batch": st.batch, "num_heads": wl.num_heads,
+                   "num_kv_heads": wl.num_kv_heads, "head_dim": wl.head_dim, "block_size": wl.block_size,
+                   "sum_context": work["sum_k"], "new_tokens": work["tokens"], "seed": wl.seed,
+                   "out_dtype": args.out_dtype, "layers_cycled": args.layers,
+                   "step": "metadata + store_kvcache + " + ("decode (split + merge)" if is_dec else "prefill")},
+        "breakdown_ms": {"metadata": round(t["meta_ms"], 5), "store": round(t["store_ms"], 5),
+                         "attention": round(t["attn_ms"], 5), "attention_median": round(t["attn_ms_median"], 5),
+                         "events_step": round(t["step_ms"], 5)},
+        "store_GBps": round(main["store_GBps"], 1),
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(wl, args.cpu_budget)
+    if secondary:
+        line["secondary"] = secondary
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())
