@@ -180,7 +180,7 @@ pa_status pa_decode(const void* q, int64_t q_tok_stride, const void* k_cache, co
     const int32_t split = split_tokens > 0 ? split_tokens
                                            : auto_split(batch, num_kv_heads, max_blocks_per_seq, block_size);
     const int32_t ms = max_splits_for(max_blocks_per_seq, block_size, split);
-    if (ms > 65535) return PA_ERR_SHAPE;
+    if (ms > 65535 || int64_t(batch) * ms * num_kv_heads > (int64_t(1) << 30)) return PA_ERR_SHAPE;
     const size_t need = pa_decode_workspace_bytes(batch, num_heads, num_kv_heads, head_dim, max_blocks_per_seq,
                                                   block_size, split);
     if (workspace_bytes < need) return PA_ERR_WORKSPACE;

@@ -19,8 +19,15 @@
 
 namespace pa {
 
-constexpr int kDecKeys = 32;       // keys per inner iteration (two 16-key score tiles)
+constexpr int kDecKeys = 32;       // keys per tile (two 16-key score tiles)
 constexpr int kVRow = 128 + 8;     // LDS row stride of the V tile, in bf16 elements (272 bytes)
+#ifndef PA_DECODE_WAVES
+#define PA_DECODE_WAVES 2
+#endif
+#ifndef PA_DECODE_NBUF
+#define PA_DECODE_NBUF 2
+#endif
+constexpr int kNBuf = PA_DECODE_NBUF;  // tiles whose loads are in flight per wave (software pipeline depth)
 
 template <bool kPow2>
 __device__ __forceinline__ int64_t slot_of_key(const int32_t* table, int key, int bs, int bs_shift) {
@@ -29,29 +36,110 @@ __device__ __forceinline__ int64_t slot_of_key(const int32_t* table, int key, in
   return int64_t(table[blk]) * bs + (key - blk * bs);
 }
 
-template <bool kPow2>
-__global__ __launch_bounds__(64) void decode_mfma_kernel(
+// One tile of K and V rows in registers. k[tt][ks]: key base + 16tt + li, d 8lg + 32ks .. +7 (the A operand of the
+// score MFMA); v[it]: key base + 4it + lg, d 8li .. +7 (staged to LDS before use).
+struct KVTile {
+  u32x4 k[2][4];
+  u32x4 v[8];
+};
+
+// Byte offsets of this lane's pieces inside a tile, the same for every tile.
+struct LaneOffsets {
+  uint32_t k;  // li * row_bytes + 16 lg
+  uint32_t v;  // lg * row_bytes + 16 li
+};
+
+__device__ __forceinline__ u32x4 ld16_off(const char* base, uint32_t off) {
+  return *reinterpret_cast<const u32x4*>(base + off);
+}
+
+// Loads the tile of keys base .. base+31 (keys >= t1 read as zero).
+//
+// kAligned (block size a multiple of 32): the tile lies in one block, so its block id is read once as a
+// wave-uniform scalar and the tile is read through a raw buffer descriptor based at the tile's first row and
+// sized to its valid rows. Rows past the end fall outside the descriptor and the hardware returns zeros for
+// them without touching memory, so there is no branch per load and the number of loads in flight is the same
+// on every path. A tile wholly past the end gets a zero-sized descriptor (based at the first tile's block, so
+// the table entry read is always a real one).
+template <bool kAligned, bool kPow2>
+__device__ __forceinline__ void load_tile(KVTile& t, const char* __restrict__ kbase, const char* __restrict__ vbase,
+                                          const int32_t* __restrict__ table, int base, int t0, int t1, int bs,
+                                          int bs_shift, int64_t row_bytes, LaneOffsets lo, int lane) {
+  const u32x4 z = {0u, 0u, 0u, 0u};
+  const int lg = lane >> 4;
+  const int li = lane & 15;
+  if (kAligned) {
+    const int n = max(0, min(kDecKeys, t1 - base));  // valid rows of this tile
+    const int key0 = n > 0 ? base : t0;
+    const int blk = kPow2 ? (key0 >> bs_shift) : (key0 / bs);
+    const int phys = __builtin_amdgcn_readfirstlane(table[blk]);
+    const int64_t tile_off = (int64_t(phys) * bs + (key0 - blk * bs)) * row_bytes;
+    const int nbytes = __builtin_amdgcn_readfirstlane(int(n * row_bytes));
+    const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<char*>(kbase + tile_off), 0, nbytes, 0x00020000);
+    const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<char*>(vbase + tile_off), 0, nbytes, 0x00020000);
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      const int off = int(lo.k) + int(16 * tt * row_bytes);
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) t.k[tt][ks] = __builtin_amdgcn_raw_buffer_load_b128(kr, off + 64 * ks, 0, 0);
+    }
+#pragma unroll
+    for (int it = 0; it < 8; ++it)
+      t.v[it] = __builtin_amdgcn_raw_buffer_load_b128(vr, int(lo.v) + int(4 * it * row_bytes), 0, 0);
+  } else {
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      const int key = base + 16 * tt + li;
+      if (key < t1) {
+        const char* kp = kbase + slot_of_key<kPow2>(table, key, bs, bs_shift) * row_bytes + 16 * lg;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) t.k[tt][ks] = ld16(kp + 64 * ks);
+      } else {
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) t.k[tt][ks] = z;
+      }
+    }
+#pragma unroll
+    for (int it = 0; it < 8; ++it) {
+      const int key = base + 4 * it + lg;
+      t.v[it] = key < t1 ? ld16(vbase + slot_of_key<kPow2>(table, key, bs, bs_shift) * row_bytes + 16 * li) : z;
+    }
+  }
+}
+
+template <bool kAligned, bool kPow2, int kHeadsPerWG>
+__global__ __launch_bounds__(64 * kHeadsPerWG) __attribute__((amdgpu_waves_per_eu(PA_DECODE_WAVES, PA_DECODE_WAVES))) void decode_mfma_kernel(
     const uint16_t* __restrict__ q, int64_t q_stride, const uint16_t* __restrict__ k_cache,
     const uint16_t* __restrict__ v_cache, const int32_t* __restrict__ ctx_lens,
     const int32_t* __restrict__ block_table, int32_t mbps, int32_t Hq, int32_t Hkv, int32_t bs, int32_t bs_shift,
     float scale_log2, void* __restrict__ out, int out_bf16, float* __restrict__ part_o,
-    float2* __restrict__ part_ml, int32_t split_tokens, int32_t max_splits) {
-  const int h = blockIdx.x;
-  const int split = blockIdx.y;
-  const int s = blockIdx.z;
+    float2* __restrict__ part_ml, int32_t split_tokens, int32_t max_splits, int32_t n_seq) {
+  // Flat grid, KV head fastest: workgroup i takes head group i % (Hkv / heads per workgroup) of work item
+  // (sequence, split) i / (Hkv / heads per workgroup). The heads of one work item are dispatched back to back
+  // and the hardware's round-robin over the 8 XCDs gives every XCD the same share of every work item.
+  const int wave = __builtin_amdgcn_readfirstlane(int(threadIdx.x >> 6));  // wave-uniform
+  const int n_hg = Hkv / kHeadsPerWG;
+  const int h = int(blockIdx.x % n_hg) * kHeadsPerWG + wave;
+  const int work = int(blockIdx.x / n_hg);
+  const int split = work % max_splits;
+  const int s = work / max_splits;
+  if (s >= n_seq) return;
   const int L = ctx_lens[s];
   const int nsplit = (L + split_tokens - 1) / split_tokens;
   if (split >= nsplit) return;
   const int t0 = split * split_tokens;
   const int t1 = min(L, t0 + split_tokens);
   const int G = Hq / Hkv;
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x & 63;
   const int lg = lane >> 4;
   const int li = lane & 15;
   const int32_t* table = block_table + int64_t(s) * mbps;
-  const int64_t row_stride = int64_t(Hkv) * 128;  // elements between consecutive slots
-  const uint16_t* kbase = k_cache + h * 128;
-  const uint16_t* vbase = v_cache + h * 128;
+  const int64_t row_bytes = int64_t(Hkv) * 256;  // bytes between consecutive slots
+  const char* kbase = reinterpret_cast<const char*>(k_cache + h * 128);
+  const char* vbase = reinterpret_cast<const char*>(v_cache + h * 128);
+  const LaneOffsets lo = {uint32_t(li * row_bytes + 16 * lg), uint32_t(lg * row_bytes + 16 * li)};
 
   // B operand of the score MFMA: lane holds Q[g = li][d = 8lg + 32ks .. +7]
   bf16x8 qb[4];
@@ -62,93 +150,86 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(
     for (int ks = 0; ks < 4; ++ks) qb[ks] = as_bf16x8(li < G ? ld16(qp + 32 * ks) : z);
   }
 
-  __shared__ __attribute__((aligned(16))) uint16_t vt[kDecKeys * kVRow];
+  // one V tile per wave; each wave only touches its own tile, and LDS accesses of one wave complete in order
+  // then start the first tiles' loads (Q is loaded first so that waiting for a tile also covers Q)
+  KVTile buf[kNBuf];
+#pragma unroll
+  for (int b = 0; b < kNBuf; ++b)
+    load_tile<kAligned, kPow2>(buf[b], kbase, vbase, table, t0 + b * kDecKeys, t0, t1, bs, bs_shift, row_bytes,
+                               lo, lane);
+
+  __shared__ __attribute__((aligned(16))) uint16_t vt_all[kHeadsPerWG][kDecKeys * kVRow];
+  uint16_t* vt = vt_all[wave];
 
   f32x4 o[8];
 #pragma unroll
   for (int mt = 0; mt < 8; ++mt) o[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m = -INFINITY;
   float lsum = 0.f;
+  // A operand rows of O^T: lane (li, lg) reads keys 4lg..4lg+3 and 16+4lg..16+4lg+3 at d = 16mt + li
+  const uint16_t* r0 = &vt[(4 * lg + (li >> 2)) * kVRow + 4 * (li & 3)];
+  const uint16_t* r1 = r0 + 16 * kVRow;
+  uint16_t* vw = &vt[lg * kVRow + 8 * li];  // this lane's V piece it goes to row 4it + lg
 
-  for (int base = t0; base < t1; base += kDecKeys) {
-    const u32x4 z = {0u, 0u, 0u, 0u};
-    // K rows for the two 16-key score tiles: lane holds K[base + 16tt + li][8lg + 32ks .. +7]
-    u32x4 kr[2][4];
+  for (int g0 = t0; g0 < t1; g0 += kNBuf * kDecKeys) {
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
-      const int key = base + 16 * tt + li;
-      if (key < t1) {
-        const uint16_t* kp = kbase + slot_of_key<kPow2>(table, key, bs, bs_shift) * row_stride + 8 * lg;
+    for (int b = 0; b < kNBuf; ++b) {
+      // Every step runs, also for a tile past the end (only possible in the last group, and only on the
+      // aligned path): its loads return zeros without touching memory, its scores are -inf and it leaves
+      // m, l and O unchanged. Unconditional steps keep the count of loads in flight the same on every path.
+      const int base = g0 + b * kDecKeys;
+      {
+        KVTile& t = buf[b];
+        // V rows to LDS (after the previous tile's transposed reads, which precede them in this wave's order)
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) kr[tt][ks] = ld16(kp + 32 * ks);
-      } else {
+        for (int it = 0; it < 8; ++it) st16(vw + 4 * it * kVRow, t.v[it]);
+        // scores: sc[tt][i] is key base + 16tt + 4lg + i, query column g = li
+        f32x4 sc[2];
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) kr[tt][ks] = z;
+        for (int tt = 0; tt < 2; ++tt) {
+          sc[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int ks = 0; ks < 4; ++ks) sc[tt] = mfma16x16x32(as_bf16x8(t.k[tt][ks]), qb[ks], sc[tt]);
+        }
+        // the registers of this tile are free: start loading the tile kNBuf tiles ahead into them
+        load_tile<kAligned, kPow2>(t, kbase, vbase, table, base + kNBuf * kDecKeys, t0, t1, bs, bs_shift,
+                                   row_bytes, lo, lane);
+        float mx = -INFINITY;
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int key = base + 16 * tt + 4 * lg + i;
+            const float v = key < t1 ? sc[tt][i] * scale_log2 : -INFINITY;
+            sc[tt][i] = v;
+            mx = fmaxf(mx, v);
+          }
+        }
+        mx = xgroup16_max(mx);
+        const float mn = fmaxf(m, mx);  // finite: the first tile holds at least one key
+        const float alpha = exp2f(m - mn);
+        m = mn;
+        float pv[8];
+        float psum = 0.f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          pv[j] = exp2f(sc[j >> 2][j & 3] - mn);
+          psum += pv[j];
+        }
+        lsum = lsum * alpha + psum;
+#pragma unroll
+        for (int mt = 0; mt < 8; ++mt) o[mt] *= alpha;
+        const u32x4 pw = {pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3]), pack_bf16x2(pv[4], pv[5]),
+                          pack_bf16x2(pv[6], pv[7])};
+        const bf16x8 pb = as_bf16x8(pw);
+#pragma unroll
+        for (int mt = 0; mt < 8; ++mt) {
+          const i16x4 a0 = lds_read_tr16(r0 + 16 * mt);
+          const i16x4 a1 = lds_read_tr16(r1 + 16 * mt);
+          const bf16x8 av = __builtin_bit_cast(bf16x8, __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7));
+          o[mt] = mfma16x16x32(av, pb, o[mt]);
+        }
       }
-    }
-    // V tile: 32 keys x 128 d as 512 pieces of 16 bytes; piece c -> key c / 16, d 8 * (c % 16)
-    u32x4 vr[8];
-#pragma unroll
-    for (int it = 0; it < 8; ++it) {
-      const int c = it * 64 + lane;
-      const int key = base + (c >> 4);
-      vr[it] = key < t1 ? ld16(vbase + slot_of_key<kPow2>(table, key, bs, bs_shift) * row_stride + 8 * (c & 15))
-                        : z;
-    }
-
-    // scores: sc[tt][i] is key base + 16tt + 4lg + i, query column g = li
-    f32x4 sc[2];
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
-      sc[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) sc[tt] = mfma16x16x32(as_bf16x8(kr[tt][ks]), qb[ks], sc[tt]);
-    }
-    float mx = -INFINITY;
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int key = base + 16 * tt + 4 * lg + i;
-        const float v = key < t1 ? sc[tt][i] * scale_log2 : -INFINITY;
-        sc[tt][i] = v;
-        mx = fmaxf(mx, v);
-      }
-    }
-    mx = xgroup16_max(mx);
-    const float mn = fmaxf(m, mx);  // finite: every tile holds at least one key
-    const float alpha = exp2f(m - mn);
-    m = mn;
-    float pv[8];
-    float psum = 0.f;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      pv[j] = exp2f(sc[j >> 2][j & 3] - mn);
-      psum += pv[j];
-    }
-    lsum = lsum * alpha + psum;
-#pragma unroll
-    for (int mt = 0; mt < 8; ++mt) o[mt] *= alpha;
-    const u32x4 pw = {pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3]), pack_bf16x2(pv[4], pv[5]),
-                      pack_bf16x2(pv[6], pv[7])};
-    const bf16x8 pb = as_bf16x8(pw);
-
-    __syncthreads();  // the previous tile's transposed reads are done
-#pragma unroll
-    for (int it = 0; it < 8; ++it) {
-      const int c = it * 64 + lane;
-      st16(&vt[(c >> 4) * kVRow + 8 * (c & 15)], vr[it]);
-    }
-    __syncthreads();
-    // A operand of O^T: lane (li, lg) needs V[key][d = 16mt + li] for keys 4lg..4lg+3 and 16+4lg..16+4lg+3
-    const uint16_t* r0 = &vt[(4 * lg + (li >> 2)) * kVRow + 4 * (li & 3)];
-    const uint16_t* r1 = r0 + 16 * kVRow;
-#pragma unroll
-    for (int mt = 0; mt < 8; ++mt) {
-      const i16x4 a0 = lds_read_tr16(r0 + 16 * mt);
-      const i16x4 a1 = lds_read_tr16(r1 + 16 * mt);
-      const bf16x8 av = __builtin_bit_cast(bf16x8, __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7));
-      o[mt] = mfma16x16x32(av, pb, o[mt]);
     }
   }
 
@@ -181,7 +262,8 @@ __global__ __launch_bounds__(64) void decode_mfma_kernel(
 }
 
 // Merge of the split partials of one (sequence, query head): M = max m_i, L = sum l_i 2^(m_i - M),
-// O = sum O_i 2^(m_i - M) / L. Sequences that fit in one split were finished by the first pass.
+// O = sum O_i 2^(m_i - M) / L. Sequences that fit in one split were finished by the first pass. Lane j first
+// holds split j's weight; the partial rows are then read four splits at a time so their loads overlap.
 __global__ __launch_bounds__(64) void decode_reduce_kernel(const int32_t* __restrict__ ctx_lens,
                                                            const float* __restrict__ part_o,
                                                            const float2* __restrict__ part_ml, int32_t Hq,
@@ -203,12 +285,29 @@ __global__ __launch_bounds__(64) void decode_reduce_kernel(const int32_t* __rest
     Ls += ml.y * exp2f(ml.x - M);
   }
   Ls = wave_sum(Ls);
+  const float* po = part_o + pi0 * 128 + 2 * lane;
   float a0 = 0.f, a1 = 0.f;
-  for (int j = 0; j < nsplit; ++j) {
-    const float w = exp2f(part_ml[pi0 + j].x - M);
-    const float2 v = *reinterpret_cast<const float2*>(part_o + (pi0 + j) * 128 + 2 * lane);
-    a0 += w * v.x;
-    a1 += w * v.y;
+  for (int j0 = 0; j0 < nsplit; j0 += 64) {
+    const float wl = j0 + lane < nsplit ? exp2f(part_ml[pi0 + j0 + lane].x - M) : 0.f;
+    const int n = min(64, nsplit - j0);
+    int j = 0;
+    for (; j + 4 <= n; j += 4) {
+      float2 v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) v[u] = *reinterpret_cast<const float2*>(po + int64_t(j0 + j + u) * 128);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const float w = __shfl(wl, j + u, 64);
+        a0 += w * v[u].x;
+        a1 += w * v[u].y;
+      }
+    }
+    for (; j < n; ++j) {
+      const float2 v = *reinterpret_cast<const float2*>(po + int64_t(j0 + j) * 128);
+      const float w = __shfl(wl, j, 64);
+      a0 += w * v.x;
+      a1 += w * v.y;
+    }
   }
   const float inv = 1.f / Ls;
   const int64_t ob = (int64_t(s) * Hq + hq) * 128 + 2 * lane;
@@ -225,23 +324,41 @@ void launch_decode_mfma(const void* q, int64_t q_stride, const void* k_cache, co
                         int32_t split_tokens, int32_t max_splits, void* workspace, hipStream_t stream) {
   float* part_o = static_cast<float*>(workspace);
   float2* part_ml = reinterpret_cast<float2*>(part_o + int64_t(batch) * Hq * max_splits * 128);
-  const dim3 grid(Hkv, max_splits, batch);
   const float sl2 = scale * kLog2e;
+  // the KV heads of one (sequence, split) run as the waves of one workgroup, so each token row of the cache is
+  // read whole (all heads) by one CU at about the same time
+#ifndef PA_DECODE_HPW
+#define PA_DECODE_HPW 1
+#endif
+  const int hpw = (Hkv % PA_DECODE_HPW == 0) ? PA_DECODE_HPW : (Hkv % 4 == 0 ? 4 : 1);
   const bool pow2 = (block_size & (block_size - 1)) == 0;
+  const bool aligned = block_size % kDecKeys == 0;  // split_tokens is a multiple of 32 too
   int shift = 0;
   while ((1 << shift) < block_size) ++shift;
   const uint16_t* qp = static_cast<const uint16_t*>(q);
   const uint16_t* kc = static_cast<const uint16_t*>(k_cache);
   const uint16_t* vc = static_cast<const uint16_t*>(v_cache);
-  if (pow2) {
-    hipLaunchKernelGGL(decode_mfma_kernel<true>, grid, dim3(64), 0, stream, qp, q_stride, kc, vc, ctx_lens,
-                       block_table, mbps, Hq, Hkv, block_size, shift, sl2, out, int(out_bf16), part_o, part_ml,
-                       split_tokens, max_splits);
-  } else {
-    hipLaunchKernelGGL(decode_mfma_kernel<false>, grid, dim3(64), 0, stream, qp, q_stride, kc, vc, ctx_lens,
-                       block_table, mbps, Hq, Hkv, block_size, shift, sl2, out, int(out_bf16), part_o, part_ml,
-                       split_tokens, max_splits);
-  }
+  const int n_hg = Hkv / hpw;
+  const int64_t n_work = int64_t(batch) * max_splits;
+  const dim3 grid(unsigned(n_hg * n_work));
+#define PA_LAUNCH_DEC(A, P)                                                                                     \
+  if (hpw == 8)                                                                                                 \
+    hipLaunchKernelGGL((decode_mfma_kernel<A, P, 8>), grid, dim3(512), 0, stream, qp, q_stride, kc, vc,          \
+                       ctx_lens, block_table, mbps, Hq, Hkv, block_size, shift, sl2, out, int(out_bf16), part_o,  \
+                       part_ml, split_tokens, max_splits, batch);                                                \
+  else if (hpw == 4)                                                                                            \
+    hipLaunchKernelGGL((decode_mfma_kernel<A, P, 4>), grid, dim3(256), 0, stream, qp, q_stride, kc, vc,          \
+                       ctx_lens, block_table, mbps, Hq, Hkv, block_size, shift, sl2, out, int(out_bf16), part_o,  \
+                       part_ml, split_tokens, max_splits, batch);                                                \
+  else                                                                                                          \
+    hipLaunchKernelGGL((decode_mfma_kernel<A, P, 1>), grid, dim3(64), 0, stream, qp, q_stride, kc, vc, ctx_lens, \
+                       block_table, mbps, Hq, Hkv, block_size, shift, sl2, out, int(out_bf16), part_o, part_ml,   \
+                       split_tokens, max_splits, batch)
+  if (aligned && pow2) PA_LAUNCH_DEC(true, true);
+  else if (aligned) PA_LAUNCH_DEC(true, false);
+  else if (pow2) PA_LAUNCH_DEC(false, true);
+  else PA_LAUNCH_DEC(false, false);
+#undef PA_LAUNCH_DEC
   if (max_splits > 1) {
     hipLaunchKernelGGL(decode_reduce_kernel, dim3(Hq, batch), dim3(64), 0, stream, ctx_lens, part_o, part_ml, Hq,
                        split_tokens, max_splits, out, int(out_bf16));
