@@ -32,6 +32,7 @@
  *   - Return value: PA_OK, or an error code for a problem the host can see before launching (nothing is
  *     launched then); PA_ERR_LAUNCH if a launch failed. batch == 0 or no tokens is a no-op returning PA_OK.
  *
+ * softmax_scale must be positive and finite (PA_ERR_SHAPE otherwise).
  * Supported: dtype PA_BF16 or PA_F32 for Q/K/V and cache (same for all); out_dtype PA_F32 or PA_BF16
  * (round to nearest even); head_dim a multiple of 8 and at most 256 (bf16, head_dim 128 and a GQA group of at
  * most 16 take the matrix-core kernels; other shapes take a plain vector kernel).

@@ -117,6 +117,7 @@ pa_status pa_prefill_varlen(const void* q, int64_t q_tok_stride, const void* k_c
     return PA_ERR_SHAPE;
   if (int64_t(num_blocks) * block_size > kInt32Max) return PA_ERR_SHAPE;
   if (q_tok_stride < int64_t(num_heads) * head_dim) return PA_ERR_SHAPE;
+  if (!(softmax_scale > 0.f) || softmax_scale > 3.0e38f) return PA_ERR_SHAPE;
   if (batch == 0 || total_q == 0) return PA_OK;
   if (max_seqlen_q <= 0 || max_blocks_per_seq <= 0 || int64_t(max_seqlen_k) > int64_t(max_blocks_per_seq) * block_size)
     return PA_ERR_SHAPE;
@@ -169,6 +170,7 @@ pa_status pa_decode(const void* q, int64_t q_tok_stride, const void* k_cache, co
     return PA_ERR_SHAPE;
   if (int64_t(num_blocks) * block_size > kInt32Max) return PA_ERR_SHAPE;
   if (q_tok_stride < int64_t(num_heads) * head_dim) return PA_ERR_SHAPE;
+  if (!(softmax_scale > 0.f) || softmax_scale > 3.0e38f) return PA_ERR_SHAPE;
   if (batch == 0) return PA_OK;
   if (max_blocks_per_seq <= 0 || batch > 65535) return PA_ERR_SHAPE;
   if (!q || !k_cache || !v_cache || !context_lens || !block_table || !out) return PA_ERR_NULL;

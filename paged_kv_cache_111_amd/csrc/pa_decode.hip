@@ -210,17 +210,13 @@ __global__ __launch_bounds__(64 * kHeadsPerWG) __attribute__((amdgpu_waves_per_e
         const float alpha = exp2f(m - mn);
         m = mn;
         float pv[8];
-        float psum = 0.f;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          pv[j] = exp2f(sc[j >> 2][j & 3] - mn);
-          psum += pv[j];
-        }
-        lsum = lsum * alpha + psum;
+        for (int j = 0; j < 8; ++j) pv[j] = exp2f(sc[j >> 2][j & 3] - mn);
 #pragma unroll
         for (int mt = 0; mt < 8; ++mt) o[mt] *= alpha;
-        const u32x4 pw = {pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3]), pack_bf16x2(pv[4], pv[5]),
-                          pack_bf16x2(pv[6], pv[7])};
+        const u32x4 pw = {pack_weights_bf16x2(pv[0], pv[1]), pack_weights_bf16x2(pv[2], pv[3]),
+                          pack_weights_bf16x2(pv[4], pv[5]), pack_weights_bf16x2(pv[6], pv[7])};
+        lsum = lsum * alpha + ((sum_bf16x2(pw[0]) + sum_bf16x2(pw[1])) + (sum_bf16x2(pw[2]) + sum_bf16x2(pw[3])));
         const bf16x8 pb = as_bf16x8(pw);
 #pragma unroll
         for (int mt = 0; mt < 8; ++mt) {

@@ -1,10 +1,12 @@
 // Paged varlen causal prefill on the matrix cores: bf16, head_dim 128.
 //
 // Workgroup = (sequence s, query head h, tile of 128 query rows); four waves of 32 rows each. Keys are walked in
-// tiles of 32 gathered through the block table into LDS (row-major, both K and V), shared by the four waves:
+// tiles of 64 gathered through the block table into LDS (row-major, both K and V, double-buffered: the next
+// tile's global loads are in flight in registers while the current tile is computed), shared by the four waves:
 //   S^T[key, q] = K[key, :] . Q[q, :]      32x32x16 MFMA, A = K rows from LDS, B = Q^T kept in registers
-//   O^T[d, q]  += V^T[d, key] P^T[key, q]  32x32x16 MFMA, A = V^T via the LDS transpose read, B = P^T kept in
-//                                           the registers the score MFMA left it in
+//   O^T[d, q]  += V^T[d, key] P^T[key, q]  32x32x16 fp16 MFMA, A = V^T via the LDS transpose read (V is
+//                                           converted to fp16 when staged), B = P^T (fp16) kept in the
+//                                           registers the score MFMA left the scores in
 // With scores transposed, each lane owns one query column, so the row max and sum need one exchange between
 // the two wave halves per tile. The key -> k-slot assignment of the second product follows the score layout
 // (lane half hh holds keys 8j + 4hh .. +3), so P^T needs no data movement.
@@ -23,9 +25,15 @@
 namespace pa {
 
 constexpr int kPreRows = 128;     // query rows per workgroup
-constexpr int kPreKeys = 32;      // keys per tile
-constexpr int kPreThreads = 256;  // four waves
+constexpr int kPreThreads = 256;  // four waves of 32 rows
 constexpr int kKRow = 128 + 8;    // LDS row stride in bf16 elements (272 bytes)
+#ifndef PA_PREFILL_KEYS
+#define PA_PREFILL_KEYS 64
+#endif
+constexpr int kPreKeys = PA_PREFILL_KEYS;  // keys per tile (a multiple of 32)
+constexpr int kSub = kPreKeys / 32;        // 32-key score sub-tiles per tile
+constexpr int kPieces = kPreKeys * 16 / kPreThreads;  // 16-byte pieces of K (and of V) per thread per tile
+constexpr float kRescaleSlack = 8.f;       // the running max is only moved when it would grow by more than this
 
 template <bool kPow2>
 __device__ __forceinline__ int64_t pf_slot(const int32_t* table, int key, int bs, int bs_shift) {
@@ -34,8 +42,66 @@ __device__ __forceinline__ int64_t pf_slot(const int32_t* table, int key, int bs
   return int64_t(table[blk]) * bs + (key - blk * bs);
 }
 
-template <bool kPow2>
-__global__ __launch_bounds__(kPreThreads) void prefill_mfma_kernel(
+// Staging registers of one K/V tile: piece c = it * 256 + tid is key c / 16, d 8 (c % 16) .. +7.
+struct PfStage {
+  u32x4 k[kPieces];
+  u32x4 v[kPieces];
+};
+
+// Global loads of the tile of keys kb .. kb + kPreKeys - 1; keys >= k_len read as zero. kAligned (block size a
+// multiple of the tile): the tile lies in one block, read through buffer descriptors sized to its valid rows.
+template <bool kAligned, bool kPow2>
+__device__ __forceinline__ void pf_gload(PfStage& st, const char* kbase, const char* vbase, const int32_t* table,
+                                         int kb, int k_len, int bs, int bs_shift, int64_t row_bytes, int tid) {
+  if (kAligned) {
+    const int n = min(kPreKeys, k_len - kb);  // >= 1
+    const int blk = kPow2 ? (kb >> bs_shift) : (kb / bs);
+    const int phys = __builtin_amdgcn_readfirstlane(table[blk]);
+    const int64_t off = (int64_t(phys) * bs + (kb - blk * bs)) * row_bytes;
+    const int nbytes = __builtin_amdgcn_readfirstlane(int(n * row_bytes));
+    const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(kbase + off), 0, nbytes,
+                                                                        0x00020000);
+    const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(vbase + off), 0, nbytes,
+                                                                        0x00020000);
+#pragma unroll
+    for (int it = 0; it < kPieces; ++it) {
+      const int c = it * kPreThreads + tid;
+      const int o = int((c >> 4) * row_bytes) + 16 * (c & 15);
+      st.k[it] = __builtin_amdgcn_raw_buffer_load_b128(kr, o, 0, 0);
+      st.v[it] = __builtin_amdgcn_raw_buffer_load_b128(vr, o, 0, 0);
+    }
+  } else {
+    const u32x4 z = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int it = 0; it < kPieces; ++it) {
+      const int c = it * kPreThreads + tid;
+      const int key = kb + (c >> 4);
+      if (key < k_len) {
+        const int64_t o = pf_slot<kPow2>(table, key, bs, bs_shift) * row_bytes + 16 * (c & 15);
+        st.k[it] = ld16(kbase + o);
+        st.v[it] = ld16(vbase + o);
+      } else {
+        st.k[it] = z;
+        st.v[it] = z;
+      }
+    }
+  }
+}
+
+// K goes to LDS as bf16; V is converted to fp16 on the way (exact in fp16's normal range), because the PV
+// product runs in fp16: its weights then carry 11 significant bits instead of bf16's 8.
+__device__ __forceinline__ void pf_lstore(const PfStage& st, uint16_t* kt, uint16_t* vt, int tid) {
+#pragma unroll
+  for (int it = 0; it < kPieces; ++it) {
+    const int c = it * kPreThreads + tid;
+    const int o = (c >> 4) * kKRow + 8 * (c & 15);
+    st16(kt + o, st.k[it]);
+    st16(vt + o, bf16x8_to_f16x8(st.v[it]));
+  }
+}
+
+template <bool kAligned, bool kPow2>
+__global__ __launch_bounds__(kPreThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_mfma_kernel(
     const uint16_t* __restrict__ q, int64_t q_stride, const uint16_t* __restrict__ k_cache,
     const uint16_t* __restrict__ v_cache, const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k,
     const int32_t* __restrict__ block_table, int32_t mbps, int32_t batch, int32_t Hq, int32_t Hkv, int32_t bs,
@@ -63,15 +129,17 @@ __global__ __launch_bounds__(kPreThreads) void prefill_mfma_kernel(
   const int n_keys = past + row_end;  // keys needed by the last row of the tile
 
   const int tid = threadIdx.x;
-  const int w = tid >> 6;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int lr = lane & 31;   // query column owned by this lane
   const int hh = lane >> 5;   // wave half
   const int my_row = row0 + 32 * w + lr;
-  const int wave_last_row = min(q_len - 1, row0 + 32 * w + 31);
-  const int wave_keys = row0 + 32 * w < q_len ? past + wave_last_row + 1 : 0;
+  const int wave_row0 = row0 + 32 * w;
+  const int wave_keys = wave_row0 < q_len ? past + min(q_len - 1, wave_row0 + 31) + 1 : 0;
   const int32_t* table = block_table + int64_t(s) * mbps;
-  const int64_t row_stride = int64_t(Hkv) * 128;
+  const int64_t row_bytes = int64_t(Hkv) * 256;
+  const char* kbase = reinterpret_cast<const char*>(k_cache + kvh * 128);
+  const char* vbase = reinterpret_cast<const char*>(v_cache + kvh * 128);
 
   // B operand of the score MFMA: lane holds Q[my_row][8hh + 16ks .. +7], ks = 0..7
   bf16x8 qb[8];
@@ -83,104 +151,114 @@ __global__ __launch_bounds__(kPreThreads) void prefill_mfma_kernel(
     for (int ks = 0; ks < 8; ++ks) qb[ks] = as_bf16x8(ok ? ld16(qp + 16 * ks) : z);
   }
 
-  __shared__ __attribute__((aligned(16))) uint16_t kt[kPreKeys * kKRow];
-  __shared__ __attribute__((aligned(16))) uint16_t vt[kPreKeys * kKRow];
+  __shared__ __attribute__((aligned(16))) uint16_t kt[2][kPreKeys * kKRow];
+  __shared__ __attribute__((aligned(16))) uint16_t vt[2][kPreKeys * kKRow];
 
   f32x16 o[4];
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
     for (int i = 0; i < 16; ++i) o[mt][i] = 0.f;
-  float m = -INFINITY;
-  float lsum = 0.f;
+  float m = -INFINITY;  // running reference max of this row, in scaled log2 units
+  float lsum = 0.f;     // this lane's part of the row sum (the two halves are added at the end)
   const int my_pos = past + my_row;
 
-  const uint16_t* kbase = k_cache + kvh * 128;
-  const uint16_t* vbase = v_cache + kvh * 128;
+  PfStage st;
+  pf_gload<kAligned, kPow2>(st, kbase, vbase, table, 0, k_len, bs, bs_shift, row_bytes, tid);
+  pf_lstore(st, kt[0], vt[0], tid);
+  __syncthreads();
 
+  // per-lane LDS read positions
+  const int li = lane & 15;
+  const int g4 = lane >> 4;
+  const int ka_off = lr * kKRow + 8 * hh;  // K A operand: row lr, d 8hh + 16ks
+  // V^T A operand through the transpose read: lane group g4 (half hh = g4 / 2, d offset 16 (g4 % 2)) reads
+  // keys 16kk + 4hh + 0..3 (slots 0..3) and 16kk + 8 + 4hh + 0..3 (slots 4..7)
+  const int va_off = (4 * (g4 >> 1) + (li >> 2)) * kKRow + 16 * (g4 & 1) + 4 * (li & 3);
+
+  int buf = 0;
   for (int kb = 0; kb < n_keys; kb += kPreKeys) {
-    // ---- cooperative gather of the K and V tiles: 2 x 512 pieces of 16 bytes; piece c -> key c/16, d 8(c%16)
-    {
-      const u32x4 z = {0u, 0u, 0u, 0u};
-      u32x4 kv[2], vv[2];
+    const bool more = kb + kPreKeys < n_keys;
+    if (more) pf_gload<kAligned, kPow2>(st, kbase, vbase, table, kb + kPreKeys, k_len, bs, bs_shift, row_bytes, tid);
+
+    if (kb < wave_keys) {
+      const uint16_t* ktb = kt[buf];
+      const uint16_t* vtb = vt[buf];
+      // ---- S^T = K Q^T: sc[sub][i] is key kb + 32 sub + 8 (i / 4) + 4 hh + (i % 4), query column lr
+      f32x16 sc[kSub];
 #pragma unroll
-      for (int it = 0; it < 2; ++it) {
-        const int c = it * kPreThreads + tid;
-        const int key = kb + (c >> 4);
-        if (key < k_len) {
-          const int64_t off = pf_slot<kPow2>(table, key, bs, bs_shift) * row_stride + 8 * (c & 15);
-          kv[it] = ld16(kbase + off);
-          vv[it] = ld16(vbase + off);
-        } else {
-          kv[it] = z;
-          vv[it] = z;
+      for (int sub = 0; sub < kSub; ++sub) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sc[sub][i] = 0.f;
+        const uint16_t* ka = ktb + ka_off + 32 * sub * kKRow;
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks)
+          sc[sub] = mfma32x32x16(as_bf16x8(*reinterpret_cast<const u32x4*>(ka + 16 * ks)), qb[ks], sc[sub]);
+      }
+      // causal mask, only where some key of the tile is after some row of this wave
+      if (kb + kPreKeys - 1 > past + wave_row0) {
+#pragma unroll
+        for (int sub = 0; sub < kSub; ++sub)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int key = kb + 32 * sub + 8 * (i >> 2) + 4 * hh + (i & 3);
+            if (key > my_pos) sc[sub][i] = -INFINITY;
+          }
+      }
+      float mx = -INFINITY;
+#pragma unroll
+      for (int sub = 0; sub < kSub; ++sub)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sc[sub][i]);
+      mx = xhalf_max(mx) * scale_log2;  // the tile's row max in scaled log2 units (-inf if all masked)
+      // The reference max only moves when the row max would exceed it by more than the slack; until then the
+      // weights exp2(s - m) stay below 2^8 and O, l need no rescaling. The result O / l does not depend on m.
+      if (__any(mx > m + kRescaleSlack)) {
+        const float mn = fmaxf(m, mx);
+        const float alpha = __builtin_amdgcn_exp2f(m - mn);  // 0 on the first tile (m = -inf)
+        m = mn;
+        lsum *= alpha;
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) o[mt] *= alpha;
+      }
+      // weights in fp16 (round to nearest); the row sum is taken over the rounded weights that enter the PV
+      // product, so the weights the output averages with sum to one
+      float psum = 0.f;
+      f16x8 pb[2 * kSub];
+#pragma unroll
+      for (int sub = 0; sub < kSub; ++sub) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sc[sub][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[sub][i], scale_log2, -m));
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+          const u32x4 pw = {pack_f16x2(sc[sub][8 * kk + 0], sc[sub][8 * kk + 1]),
+                            pack_f16x2(sc[sub][8 * kk + 2], sc[sub][8 * kk + 3]),
+                            pack_f16x2(sc[sub][8 * kk + 4], sc[sub][8 * kk + 5]),
+                            pack_f16x2(sc[sub][8 * kk + 6], sc[sub][8 * kk + 7])};
+          psum = add_f16x2(pw[3], add_f16x2(pw[2], add_f16x2(pw[1], add_f16x2(pw[0], psum))));
+          pb[2 * sub + kk] = as_f16x8(pw);
         }
       }
-      __syncthreads();  // previous tile fully consumed
+      lsum += psum;
+      // ---- O^T += V^T P^T
 #pragma unroll
-      for (int it = 0; it < 2; ++it) {
-        const int c = it * kPreThreads + tid;
-        st16(&kt[(c >> 4) * kKRow + 8 * (c & 15)], kv[it]);
-        st16(&vt[(c >> 4) * kKRow + 8 * (c & 15)], vv[it]);
-      }
-      __syncthreads();
-    }
-    if (kb >= wave_keys) continue;  // every row of this wave is before this tile
-
-    // ---- S^T = K Q^T: sc[i] is key kb + 8(i/4) + 4hh + (i%4), query column lr
-    f32x16 sc;
+      for (int sub = 0; sub < kSub; ++sub) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) sc[i] = 0.f;
-    const uint16_t* ka = &kt[lr * kKRow + 8 * hh];
+        for (int kk = 0; kk < 2; ++kk) {
+          const uint16_t* vr = vtb + va_off + (32 * sub + 16 * kk) * kKRow;
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) sc = mfma32x32x16(as_bf16x8(*reinterpret_cast<const u32x4*>(ka + 16 * ks)), qb[ks], sc);
-
-    float mx = -INFINITY;
-    const bool need_mask = kb + kPreKeys - 1 > past + row0 + 32 * w;  // some key of the tile is after some row
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int key = kb + 8 * (i >> 2) + 4 * hh + (i & 3);
-      float v = sc[i] * scale_log2;
-      if (need_mask && key > my_pos) v = -INFINITY;
-      sc[i] = v;
-      mx = fmaxf(mx, v);
-    }
-    mx = xhalf_max(mx);
-    const float mn = fmaxf(m, mx);  // finite: key 0 is visible to every row
-    const float alpha = exp2f(m - mn);
-    m = mn;
-    float psum = 0.f;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      sc[i] = exp2f(sc[i] - mn);
-      psum += sc[i];
-    }
-    lsum = lsum * alpha + psum;
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) o[mt] *= alpha;
-    bf16x8 pb[2];
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      const u32x4 pw = {pack_bf16x2(sc[8 * kk + 0], sc[8 * kk + 1]), pack_bf16x2(sc[8 * kk + 2], sc[8 * kk + 3]),
-                        pack_bf16x2(sc[8 * kk + 4], sc[8 * kk + 5]), pack_bf16x2(sc[8 * kk + 6], sc[8 * kk + 7])};
-      pb[kk] = as_bf16x8(pw);
-    }
-
-    // ---- O^T += V^T P^T. Lane group g4 = lane/16: half hh = g4/2, d offset 16(g4%2). For k-step kk the lane's
-    // slots 0..3 are keys 16kk + 4hh + 0..3 and slots 4..7 keys 16kk + 8 + 4hh + 0..3.
-    const int li = lane & 15;
-    const int g4 = lane >> 4;
-    const uint16_t* vr = &vt[(4 * (g4 >> 1) + (li >> 2)) * kKRow + 16 * (g4 & 1) + 4 * (li & 3)];
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
-        const i16x4 a0 = lds_read_tr16(vr + (16 * kk) * kKRow + 32 * mt);
-        const i16x4 a1 = lds_read_tr16(vr + (16 * kk + 8) * kKRow + 32 * mt);
-        const bf16x8 av = __builtin_bit_cast(bf16x8, __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7));
-        o[mt] = mfma32x32x16(av, pb[kk], o[mt]);
+          for (int mt = 0; mt < 4; ++mt) {
+            const i16x4 a0 = lds_read_tr16(vr + 32 * mt);
+            const i16x4 a1 = lds_read_tr16(vr + 8 * kKRow + 32 * mt);
+            const f16x8 av = __builtin_bit_cast(f16x8, __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7));
+            o[mt] = mfma32x32x16_f16(av, pb[2 * sub + kk], o[mt]);
+          }
+        }
       }
     }
+    if (more) pf_lstore(st, kt[buf ^ 1], vt[buf ^ 1], tid);
+    __syncthreads();
+    buf ^= 1;
   }
 
   if (my_row >= q_len) return;
@@ -215,20 +293,21 @@ void launch_prefill_mfma(const void* q, int64_t q_stride, const void* k_cache, c
   const int grid = ((n_work + 7) / 8) * 8;
   const float sl2 = scale * kLog2e;
   const bool pow2 = (block_size & (block_size - 1)) == 0;
+  const bool aligned = block_size % kPreKeys == 0;
   int shift = 0;
   while ((1 << shift) < block_size) ++shift;
   const uint16_t* qp = static_cast<const uint16_t*>(q);
   const uint16_t* kc = static_cast<const uint16_t*>(k_cache);
   const uint16_t* vc = static_cast<const uint16_t*>(v_cache);
-  if (pow2) {
-    hipLaunchKernelGGL(prefill_mfma_kernel<true>, dim3(grid), dim3(kPreThreads), 0, stream, qp, q_stride, kc, vc,
-                       cu_q, cu_k, block_table, mbps, batch, Hq, Hkv, block_size, shift, sl2, out, int(out_bf16),
-                       n_qtiles, n_work);
-  } else {
-    hipLaunchKernelGGL(prefill_mfma_kernel<false>, dim3(grid), dim3(kPreThreads), 0, stream, qp, q_stride, kc, vc,
-                       cu_q, cu_k, block_table, mbps, batch, Hq, Hkv, block_size, shift, sl2, out, int(out_bf16),
-                       n_qtiles, n_work);
-  }
+#define PA_LAUNCH_PF(A, P)                                                                                      \
+  hipLaunchKernelGGL((prefill_mfma_kernel<A, P>), dim3(grid), dim3(kPreThreads), 0, stream, qp, q_stride, kc, vc, \
+                     cu_q, cu_k, block_table, mbps, batch, Hq, Hkv, block_size, shift, sl2, out, int(out_bf16),  \
+                     n_qtiles, n_work)
+  if (aligned && pow2) PA_LAUNCH_PF(true, true);
+  else if (aligned) PA_LAUNCH_PF(true, false);
+  else if (pow2) PA_LAUNCH_PF(false, true);
+  else PA_LAUNCH_PF(false, false);
+#undef PA_LAUNCH_PF
 }
 
 }  // namespace pa

@@ -128,3 +128,11 @@ def test_binding_checks_layouts_on_the_host():
 
 def test_ctypes_signatures_cover_pointer_widths():
     assert ctypes.sizeof(ctypes.c_void_p) == 8
+
+
+def test_nonpositive_scale_is_rejected():
+    assert _prefill(scale=0.0) == b.PA_ERR_SHAPE
+    assert _prefill(scale=-0.1) == b.PA_ERR_SHAPE
+    assert _prefill(scale=float("nan")) == b.PA_ERR_SHAPE
+    assert _decode(scale=0.0) == b.PA_ERR_SHAPE
+    assert _decode(scale=float("inf")) == b.PA_ERR_SHAPE

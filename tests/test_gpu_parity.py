@@ -33,7 +33,9 @@ def _run_and_check(wl, out_dtype=torch.float32, split_tokens=0, seqs=None, rows=
             assert np.array_equal(to_host_bits(kc), kc_h), "K cache differs after store"
             assert np.array_equal(to_host_bits(vc), vc_h), "V cache differs after store"
         frows = None if seqs is None else flat_rows(meta_r, seqs, rows)
-        errs.append(assert_close(out, ref, frows, what=f"{wl.name} step {i}"))
+        err = assert_close(out, ref, frows, what=f"{wl.name} step {i}")
+        print(f"[err] {wl.name} step {i}: max_abs {err[0]:.3e} rel_rms {err[1]:.3e}", flush=True)
+        errs.append(err)
     return errs
 
 
