@@ -304,7 +304,7 @@ def main() -> int:
     t = main["timing"]
     work = main["work"]
     is_dec = main["kind"] == "decode"
-    sha = _src_sha("pa_decode.hip") if is_dec else _src_sha("pa_prefill.hip")
+    sha = _src_sha("pa_decode.hip", "pa_common.h") if is_dec else _src_sha("pa_prefill.hip", "pa_common.h")
     traffic = _traffic(f"{main_name}_hbm_traffic.json", sha)
     if is_dec:
         value = main["step_GBps"]
