@@ -20,13 +20,18 @@
 // eighth) get consecutive logical ids, and the logical order is (KV head, sequence, query tile from the last,
 // query head in the group). The G query heads that share a KV head, and the query tiles of that head, then run
 // on one XCD and read the same K/V through its L2; the heaviest (last) tiles of each sequence start first.
+#include <type_traits>
+
 #include "pa_launch.h"
 
 namespace pa {
 
 constexpr int kPreRows = 128;     // query rows per workgroup
 constexpr int kPreThreads = 256;  // four waves of 32 rows
-constexpr int kKRow = 128 + 8;    // LDS row stride in bf16 elements (272 bytes)
+constexpr int kKRow = 128 + 8;    // LDS row stride of the K tile, in elements (272 bytes: 16-byte reads of
+                                  // consecutive rows land 4 banks apart)
+constexpr int kVRow = 128 + 16;   // LDS row stride of the V tile (288 bytes: the transposed 8-byte reads of 4
+                                  // consecutive rows land 8 banks apart)
 #ifndef PA_PREFILL_KEYS
 #define PA_PREFILL_KEYS 64
 #endif
@@ -42,33 +47,30 @@ __device__ __forceinline__ int64_t pf_slot(const int32_t* table, int key, int bs
   return int64_t(table[blk]) * bs + (key - blk * bs);
 }
 
-// Staging registers of one K/V tile: piece c = it * 256 + tid is key c / 16, d 8 (c % 16) .. +7.
-struct PfStage {
-  u32x4 k[kPieces];
-  u32x4 v[kPieces];
-};
+// Buffer descriptor over the valid rows of the tile of keys kb .. kb + kPreKeys - 1 (kAligned case).
+template <bool kPow2>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t pf_tile_rsrc(const char* base, const int32_t* table, int kb,
+                                                              int k_len, int bs, int bs_shift, int64_t row_bytes) {
+  const int n = max(0, min(kPreKeys, k_len - kb));
+  const int key0 = n > 0 ? kb : 0;
+  const int blk = kPow2 ? (key0 >> bs_shift) : (key0 / bs);
+  const int phys = __builtin_amdgcn_readfirstlane(table[blk]);
+  const int64_t off = (int64_t(phys) * bs + (key0 - blk * bs)) * row_bytes;
+  const int nbytes = __builtin_amdgcn_readfirstlane(int(n * row_bytes));
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base + off), 0, nbytes, 0x00020000);
+}
 
-// Global loads of the tile of keys kb .. kb + kPreKeys - 1; keys >= k_len read as zero. kAligned (block size a
-// multiple of the tile): the tile lies in one block, read through buffer descriptors sized to its valid rows.
+// Global loads of one tile (K or V) into staging registers: piece c = it * 256 + tid is key c / 16,
+// d 8 (c % 16) .. +7. Keys >= k_len (and tiles wholly past the end) read as zero.
 template <bool kAligned, bool kPow2>
-__device__ __forceinline__ void pf_gload(PfStage& st, const char* kbase, const char* vbase, const int32_t* table,
-                                         int kb, int k_len, int bs, int bs_shift, int64_t row_bytes, int tid) {
+__device__ __forceinline__ void pf_gload1(u32x4* dst, const char* base, const int32_t* table, int kb, int k_len,
+                                          int bs, int bs_shift, int64_t row_bytes, int tid) {
   if (kAligned) {
-    const int n = min(kPreKeys, k_len - kb);  // >= 1
-    const int blk = kPow2 ? (kb >> bs_shift) : (kb / bs);
-    const int phys = __builtin_amdgcn_readfirstlane(table[blk]);
-    const int64_t off = (int64_t(phys) * bs + (kb - blk * bs)) * row_bytes;
-    const int nbytes = __builtin_amdgcn_readfirstlane(int(n * row_bytes));
-    const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(kbase + off), 0, nbytes,
-                                                                        0x00020000);
-    const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(vbase + off), 0, nbytes,
-                                                                        0x00020000);
+    const __amdgpu_buffer_rsrc_t r = pf_tile_rsrc<kPow2>(base, table, kb, k_len, bs, bs_shift, row_bytes);
 #pragma unroll
     for (int it = 0; it < kPieces; ++it) {
       const int c = it * kPreThreads + tid;
-      const int o = int((c >> 4) * row_bytes) + 16 * (c & 15);
-      st.k[it] = __builtin_amdgcn_raw_buffer_load_b128(kr, o, 0, 0);
-      st.v[it] = __builtin_amdgcn_raw_buffer_load_b128(vr, o, 0, 0);
+      dst[it] = __builtin_amdgcn_raw_buffer_load_b128(r, int((c >> 4) * row_bytes) + 16 * (c & 15), 0, 0);
     }
   } else {
     const u32x4 z = {0u, 0u, 0u, 0u};
@@ -76,27 +78,105 @@ __device__ __forceinline__ void pf_gload(PfStage& st, const char* kbase, const c
     for (int it = 0; it < kPieces; ++it) {
       const int c = it * kPreThreads + tid;
       const int key = kb + (c >> 4);
-      if (key < k_len) {
-        const int64_t o = pf_slot<kPow2>(table, key, bs, bs_shift) * row_bytes + 16 * (c & 15);
-        st.k[it] = ld16(kbase + o);
-        st.v[it] = ld16(vbase + o);
-      } else {
-        st.k[it] = z;
-        st.v[it] = z;
-      }
+      dst[it] = key < k_len ? ld16(base + pf_slot<kPow2>(table, key, bs, bs_shift) * row_bytes + 16 * (c & 15)) : z;
     }
   }
 }
 
-// K goes to LDS as bf16; V is converted to fp16 on the way (exact in fp16's normal range), because the PV
-// product runs in fp16: its weights then carry 11 significant bits instead of bf16's 8.
-__device__ __forceinline__ void pf_lstore(const PfStage& st, uint16_t* kt, uint16_t* vt, int tid) {
+__device__ __forceinline__ void pf_lstore_k(const u32x4* src, uint16_t* kt, int tid) {
 #pragma unroll
   for (int it = 0; it < kPieces; ++it) {
     const int c = it * kPreThreads + tid;
-    const int o = (c >> 4) * kKRow + 8 * (c & 15);
-    st16(kt + o, st.k[it]);
-    st16(vt + o, bf16x8_to_f16x8(st.v[it]));
+    st16(kt + (c >> 4) * kKRow + 8 * (c & 15), src[it]);
+  }
+}
+
+// V is converted to fp16 on the way to LDS (exact in fp16's normal range): the PV product runs in fp16.
+__device__ __forceinline__ void pf_lstore_v(const u32x4* src, uint16_t* vt, int tid) {
+#pragma unroll
+  for (int it = 0; it < kPieces; ++it) {
+    const int c = it * kPreThreads + tid;
+    st16(vt + (c >> 4) * kVRow + 8 * (c & 15), bf16x8_to_f16x8(src[it]));
+  }
+}
+
+// S^T for the 64 keys of a K tile in LDS: sc[sub][i] is key 32 sub + 8 (i / 4) + 4 hh + (i % 4) of the tile,
+// query column lr of the wave.
+__device__ __forceinline__ void pf_scores(f32x16 (&sc)[kSub], const uint16_t* kt, int ka_off, const bf16x8 (&qb)[8]) {
+#pragma unroll
+  for (int sub = 0; sub < kSub; ++sub) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) sc[sub][i] = 0.f;
+    const uint16_t* ka = kt + ka_off + 32 * sub * kKRow;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks)
+      sc[sub] = mfma32x32x16(as_bf16x8(*reinterpret_cast<const u32x4*>(ka + 16 * ks)), qb[ks], sc[sub]);
+  }
+}
+
+// Online softmax of one tile's scores (mask, running max, weights) and O^T += V^T P^T from the V tile in LDS.
+__device__ __forceinline__ void pf_softmax_pv(f32x16 (&sc)[kSub], f32x16 (&o)[4], float& m, float& lsum,
+                                              const uint16_t* vt, int va_off, int kb, bool need_mask, int my_pos,
+                                              int hh, float scale_log2) {
+  if (need_mask) {
+#pragma unroll
+    for (int sub = 0; sub < kSub; ++sub)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int key = kb + 32 * sub + 8 * (i >> 2) + 4 * hh + (i & 3);
+        if (key > my_pos) sc[sub][i] = -INFINITY;
+      }
+  }
+  float mx = -INFINITY;
+#pragma unroll
+  for (int sub = 0; sub < kSub; ++sub)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sc[sub][i]);
+  mx = xhalf_max(mx) * scale_log2;  // the tile's row max in scaled log2 units (-inf if all masked)
+  // The reference max only moves when the row max would exceed it by more than the slack; until then the
+  // weights exp2(s - m) stay below 2^8 and O, l need no rescaling. The result O / l does not depend on m.
+  if (__any(mx > m + kRescaleSlack)) {
+    const float mn = fmaxf(m, mx);
+    const float alpha = __builtin_amdgcn_exp2f(m - mn);  // 0 on the first tile (m = -inf)
+    m = mn;
+    lsum *= alpha;
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) o[mt] *= alpha;
+  }
+  // weights in fp16 (round to nearest); the row sum is taken over the rounded weights that enter the PV
+  // product, so the weights the output averages with sum to one
+  float psum = 0.f;
+  f16x8 pb[2 * kSub];
+#pragma unroll
+  for (int sub = 0; sub < kSub; ++sub) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) sc[sub][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[sub][i], scale_log2, -m));
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const u32x4 pw = {pack_f16x2(sc[sub][8 * kk + 0], sc[sub][8 * kk + 1]),
+                        pack_f16x2(sc[sub][8 * kk + 2], sc[sub][8 * kk + 3]),
+                        pack_f16x2(sc[sub][8 * kk + 4], sc[sub][8 * kk + 5]),
+                        pack_f16x2(sc[sub][8 * kk + 6], sc[sub][8 * kk + 7])};
+      psum = add_f16x2(pw[3], add_f16x2(pw[2], add_f16x2(pw[1], add_f16x2(pw[0], psum))));
+      pb[2 * sub + kk] = as_f16x8(pw);
+    }
+  }
+  lsum += psum;
+  // O^T += V^T P^T. Lane group g4 = lane / 16 (half hh = g4 / 2, d offset 16 (g4 % 2)); for k-step kk the lane's
+  // slots 0..3 are keys 16 kk + 4 hh + 0..3 and slots 4..7 keys 16 kk + 8 + 4 hh + 0..3.
+#pragma unroll
+  for (int sub = 0; sub < kSub; ++sub) {
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const uint16_t* vr = vt + va_off + (32 * sub + 16 * kk) * kVRow;
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        const i16x4 a0 = lds_read_tr16(vr + 32 * mt);
+        const i16x4 a1 = lds_read_tr16(vr + 8 * kVRow + 32 * mt);
+        const f16x8 av = __builtin_bit_cast(f16x8, __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7));
+        o[mt] = mfma32x32x16_f16(av, pb[2 * sub + kk], o[mt]);
+      }
+    }
   }
 }
 
@@ -127,6 +207,7 @@ __global__ __launch_bounds__(kPreThreads) __attribute__((amdgpu_waves_per_eu(2, 
   const int past = k_len - q_len;  // position of row 0
   const int row_end = min(q_len, row0 + kPreRows);
   const int n_keys = past + row_end;  // keys needed by the last row of the tile
+  const int n_tiles = (n_keys + kPreKeys - 1) / kPreKeys;
 
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -136,10 +217,12 @@ __global__ __launch_bounds__(kPreThreads) __attribute__((amdgpu_waves_per_eu(2, 
   const int my_row = row0 + 32 * w + lr;
   const int wave_row0 = row0 + 32 * w;
   const int wave_keys = wave_row0 < q_len ? past + min(q_len - 1, wave_row0 + 31) + 1 : 0;
+  const int wave_tiles = (wave_keys + kPreKeys - 1) / kPreKeys;  // the tiles this wave computes: 0 .. wave_tiles-1
   const int32_t* table = block_table + int64_t(s) * mbps;
   const int64_t row_bytes = int64_t(Hkv) * 256;
   const char* kbase = reinterpret_cast<const char*>(k_cache + kvh * 128);
   const char* vbase = reinterpret_cast<const char*>(v_cache + kvh * 128);
+  const int my_pos = past + my_row;
 
   // B operand of the score MFMA: lane holds Q[my_row][8hh + 16ks .. +7], ks = 0..7
   bf16x8 qb[8];
@@ -151,8 +234,10 @@ __global__ __launch_bounds__(kPreThreads) __attribute__((amdgpu_waves_per_eu(2, 
     for (int ks = 0; ks < 8; ++ks) qb[ks] = as_bf16x8(ok ? ld16(qp + 16 * ks) : z);
   }
 
+  // K tiles run one tile ahead of V tiles: while tile j's softmax and PV run, tile j+1's scores are already
+  // being computed (so the matrix cores work during the softmax) and K tile j+2 / V tile j+1 are loading.
   __shared__ __attribute__((aligned(16))) uint16_t kt[2][kPreKeys * kKRow];
-  __shared__ __attribute__((aligned(16))) uint16_t vt[2][kPreKeys * kKRow];
+  __shared__ __attribute__((aligned(16))) uint16_t vt[2][kPreKeys * kVRow];
 
   f32x16 o[4];
 #pragma unroll
@@ -161,104 +246,42 @@ __global__ __launch_bounds__(kPreThreads) __attribute__((amdgpu_waves_per_eu(2, 
     for (int i = 0; i < 16; ++i) o[mt][i] = 0.f;
   float m = -INFINITY;  // running reference max of this row, in scaled log2 units
   float lsum = 0.f;     // this lane's part of the row sum (the two halves are added at the end)
-  const int my_pos = past + my_row;
 
-  PfStage st;
-  pf_gload<kAligned, kPow2>(st, kbase, vbase, table, 0, k_len, bs, bs_shift, row_bytes, tid);
-  pf_lstore(st, kt[0], vt[0], tid);
-  __syncthreads();
-
-  // per-lane LDS read positions
   const int li = lane & 15;
   const int g4 = lane >> 4;
   const int ka_off = lr * kKRow + 8 * hh;  // K A operand: row lr, d 8hh + 16ks
-  // V^T A operand through the transpose read: lane group g4 (half hh = g4 / 2, d offset 16 (g4 % 2)) reads
-  // keys 16kk + 4hh + 0..3 (slots 0..3) and 16kk + 8 + 4hh + 0..3 (slots 4..7)
-  const int va_off = (4 * (g4 >> 1) + (li >> 2)) * kKRow + 16 * (g4 & 1) + 4 * (li & 3);
+  const int va_off = (4 * (g4 >> 1) + (li >> 2)) * kVRow + 16 * (g4 & 1) + 4 * (li & 3);
 
-  int buf = 0;
-  for (int kb = 0; kb < n_keys; kb += kPreKeys) {
-    const bool more = kb + kPreKeys < n_keys;
-    if (more) pf_gload<kAligned, kPow2>(st, kbase, vbase, table, kb + kPreKeys, k_len, bs, bs_shift, row_bytes, tid);
+  u32x4 kst[kPieces], vst[kPieces];
+  // prologue: K tiles 0 and 1, V tile 0 in LDS; scores of tile 0
+  pf_gload1<kAligned, kPow2>(kst, kbase, table, 0, k_len, bs, bs_shift, row_bytes, tid);
+  pf_gload1<kAligned, kPow2>(vst, vbase, table, 0, k_len, bs, bs_shift, row_bytes, tid);
+  pf_lstore_k(kst, kt[0], tid);
+  pf_lstore_v(vst, vt[0], tid);
+  pf_gload1<kAligned, kPow2>(kst, kbase, table, kPreKeys, k_len, bs, bs_shift, row_bytes, tid);
+  pf_lstore_k(kst, kt[1], tid);
+  __syncthreads();
+  f32x16 sa[kSub], sb[kSub];
+  if (wave_tiles > 0) pf_scores(sa, kt[0], ka_off, qb);
+  __syncthreads();  // K tile 0 has been read by every wave before iteration 0 replaces it
 
-    if (kb < wave_keys) {
-      const uint16_t* ktb = kt[buf];
-      const uint16_t* vtb = vt[buf];
-      // ---- S^T = K Q^T: sc[sub][i] is key kb + 32 sub + 8 (i / 4) + 4 hh + (i % 4), query column lr
-      f32x16 sc[kSub];
-#pragma unroll
-      for (int sub = 0; sub < kSub; ++sub) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) sc[sub][i] = 0.f;
-        const uint16_t* ka = ktb + ka_off + 32 * sub * kKRow;
-#pragma unroll
-        for (int ks = 0; ks < 8; ++ks)
-          sc[sub] = mfma32x32x16(as_bf16x8(*reinterpret_cast<const u32x4*>(ka + 16 * ks)), qb[ks], sc[sub]);
-      }
-      // causal mask, only where some key of the tile is after some row of this wave
-      if (kb + kPreKeys - 1 > past + wave_row0) {
-#pragma unroll
-        for (int sub = 0; sub < kSub; ++sub)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int key = kb + 32 * sub + 8 * (i >> 2) + 4 * hh + (i & 3);
-            if (key > my_pos) sc[sub][i] = -INFINITY;
-          }
-      }
-      float mx = -INFINITY;
-#pragma unroll
-      for (int sub = 0; sub < kSub; ++sub)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sc[sub][i]);
-      mx = xhalf_max(mx) * scale_log2;  // the tile's row max in scaled log2 units (-inf if all masked)
-      // The reference max only moves when the row max would exceed it by more than the slack; until then the
-      // weights exp2(s - m) stay below 2^8 and O, l need no rescaling. The result O / l does not depend on m.
-      if (__any(mx > m + kRescaleSlack)) {
-        const float mn = fmaxf(m, mx);
-        const float alpha = __builtin_amdgcn_exp2f(m - mn);  // 0 on the first tile (m = -inf)
-        m = mn;
-        lsum *= alpha;
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt) o[mt] *= alpha;
-      }
-      // weights in fp16 (round to nearest); the row sum is taken over the rounded weights that enter the PV
-      // product, so the weights the output averages with sum to one
-      float psum = 0.f;
-      f16x8 pb[2 * kSub];
-#pragma unroll
-      for (int sub = 0; sub < kSub; ++sub) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) sc[sub][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[sub][i], scale_log2, -m));
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-          const u32x4 pw = {pack_f16x2(sc[sub][8 * kk + 0], sc[sub][8 * kk + 1]),
-                            pack_f16x2(sc[sub][8 * kk + 2], sc[sub][8 * kk + 3]),
-                            pack_f16x2(sc[sub][8 * kk + 4], sc[sub][8 * kk + 5]),
-                            pack_f16x2(sc[sub][8 * kk + 6], sc[sub][8 * kk + 7])};
-          psum = add_f16x2(pw[3], add_f16x2(pw[2], add_f16x2(pw[1], add_f16x2(pw[0], psum))));
-          pb[2 * sub + kk] = as_f16x8(pw);
-        }
-      }
-      lsum += psum;
-      // ---- O^T += V^T P^T
-#pragma unroll
-      for (int sub = 0; sub < kSub; ++sub) {
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-          const uint16_t* vr = vtb + va_off + (32 * sub + 16 * kk) * kKRow;
-#pragma unroll
-          for (int mt = 0; mt < 4; ++mt) {
-            const i16x4 a0 = lds_read_tr16(vr + 32 * mt);
-            const i16x4 a1 = lds_read_tr16(vr + 8 * kKRow + 32 * mt);
-            const f16x8 av = __builtin_bit_cast(f16x8, __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7));
-            o[mt] = mfma32x32x16_f16(av, pb[2 * sub + kk], o[mt]);
-          }
-        }
-      }
-    }
-    if (more) pf_lstore(st, kt[buf ^ 1], vt[buf ^ 1], tid);
+  auto step = [&](int j, f32x16 (&cur)[kSub], f32x16 (&nxt)[kSub], auto par) {
+    constexpr int P = decltype(par)::value;  // j % 2
+    const int kb = j * kPreKeys;
+    // K tile j+2 and V tile j+1 start loading (past the end they read as zero and touch no memory)
+    pf_gload1<kAligned, kPow2>(kst, kbase, table, kb + 2 * kPreKeys, k_len, bs, bs_shift, row_bytes, tid);
+    pf_gload1<kAligned, kPow2>(vst, vbase, table, kb + kPreKeys, k_len, bs, bs_shift, row_bytes, tid);
+    if (j + 1 < wave_tiles) pf_scores(nxt, kt[1 - P], ka_off, qb);
+    if (j < wave_tiles)
+      pf_softmax_pv(cur, o, m, lsum, vt[P], va_off, kb, kb + kPreKeys - 1 > past + wave_row0, my_pos, hh,
+                    scale_log2);
+    pf_lstore_k(kst, kt[P], tid);      // K tile j was last read in the previous step
+    pf_lstore_v(vst, vt[1 - P], tid);  // V tile j-1 was last read in the previous step
     __syncthreads();
-    buf ^= 1;
+  };
+  for (int j = 0; j < n_tiles; j += 2) {
+    step(j, sa, sb, std::integral_constant<int, 0>());
+    if (j + 1 < n_tiles) step(j + 1, sb, sa, std::integral_constant<int, 1>());
   }
 
   if (my_row >= q_len) return;
