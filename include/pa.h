@@ -131,9 +131,13 @@ size_t pa_prefill_workspace_bytes(int32_t batch, int32_t num_heads, int32_t head
 /*
  * pa_decode -- one query token per sequence over its context_lens[s] cached keys (the new token included).
  *
- * Same arithmetic as prefill with q_len = 1 (the query at position context_lens[s] - 1 sees every key). The
- * keys are cut into splits of split_tokens; each split yields an unnormalised partial output with its running
- * max and sum, and a second pass merges the partials of a sequence with the log-sum-exp rule. FlashAttention's
+ * Same arithmetic as prefill with q_len = 1 (the query at position context_lens[s] - 1 sees every key). With
+ * split_tokens > 0 the keys of each sequence are cut into splits of split_tokens; each split yields an
+ * unnormalised partial output with its running max and sum, and a second pass merges the partials of a sequence
+ * with the log-sum-exp rule. With split_tokens == 0 the library chooses: for head_dim 128, at most 16 query heads
+ * per KV head and a block_size that is a multiple of 32, a balanced decode (a fixed set of workers, each taking an
+ * equal share of all (KV head, key) work, partials of cut sequences merged the same way); otherwise splits of
+ * pa_decode_split_tokens(...) keys. Results agree to rounding whatever the split. FlashAttention's
  * KV-cache format: q (batch, 1, nheads, headdim), cache_seqlens, block_tables ("Nano-vLLM 架构详解" §3.2).
  *   q            (device) [batch, num_heads, head_dim]; sequence s starts at element s * q_tok_stride
  *   context_lens (device) [batch], each >= 1 and <= max_blocks_per_seq * block_size
@@ -148,7 +152,8 @@ pa_status pa_decode(const void* q, int64_t q_tok_stride, const void* k_cache, co
                     int32_t block_size, float softmax_scale, pa_dtype dtype, void* out, pa_dtype out_dtype,
                     int32_t split_tokens, void* workspace, size_t workspace_bytes, void* stream);
 
-/* Keys per split pa_decode uses for these host sizes when split_tokens == 0. */
+/* Keys per split pa_decode uses for these host sizes when split_tokens == 0 and the balanced decode does not
+ * apply. */
 int32_t pa_decode_split_tokens(int32_t batch, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
                                int32_t max_blocks_per_seq, int32_t block_size);
 

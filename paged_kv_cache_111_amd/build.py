@@ -14,7 +14,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libpa.so")
-SOURCES = ["pa_api.hip", "pa_meta_store.hip", "pa_generic.hip", "pa_decode.hip", "pa_prefill.hip"]
+SOURCES = ["pa_api.hip", "pa_meta_store.hip", "pa_generic.hip", "pa_decode.hip", "pa_decode_stream.hip",
+           "pa_prefill.hip"]
 ARCH = "gfx950"
 
 # Packed fp32 VALU instructions are kept out of every kernel (plain float code only).

@@ -38,6 +38,25 @@ bool decode_uses_mfma(pa_dtype dtype, int32_t Hq, int32_t Hkv, int32_t D) {
   return dtype == PA_BF16 && D == 128 && Hq / Hkv <= 16;
 }
 
+// Workers of the balanced decode (split_tokens == 0): two rounds of two waves per SIMD of the 256 CUs (measured
+// faster than one round on long contexts, equal on short ones).
+#ifndef PA_STREAM_WORKERS
+#define PA_STREAM_WORKERS 4096
+#endif
+constexpr int32_t kStreamWorkers = PA_STREAM_WORKERS;
+
+// The balanced decode takes shapes whose 32-key tiles never straddle a block (and the batch its prefix sums
+// can hold in LDS).
+// The balanced decode takes split_tokens == 0 when its kernel fits the sizes: D = 128, at most 16 query heads per
+// KV head (one partial slot holds 16 rows), 32-key tiles inside a block, and padded lengths whose sum over the
+// batch fits the int32 prefix sums.
+bool decode_uses_stream(int32_t split_tokens, int32_t Hq, int32_t Hkv, int32_t D, int32_t mbps, int32_t block_size,
+                        int32_t batch) {
+  const int64_t padded_max = (int64_t(mbps) * block_size + 31) & ~int64_t(31);
+  return split_tokens == 0 && D == 128 && Hq / Hkv <= 16 && block_size % 32 == 0 && batch <= 4096 &&
+         int64_t(batch) * padded_max < (int64_t(1) << 31);
+}
+
 }  // namespace
 
 extern "C" {
@@ -152,6 +171,8 @@ size_t pa_decode_workspace_bytes(int32_t batch, int32_t num_heads, int32_t num_k
   if (batch <= 0 || num_heads <= 0 || num_kv_heads <= 0 || head_dim <= 0 || max_blocks_per_seq <= 0 ||
       block_size <= 0 || split_tokens < 0)
     return 0;
+  if (decode_uses_stream(split_tokens, num_heads, num_kv_heads, head_dim, max_blocks_per_seq, block_size, batch))
+    return pa::decode_stream_workspace_bytes(kStreamWorkers);
   const int32_t split = split_tokens > 0 ? split_tokens
                                          : auto_split(batch, num_kv_heads, max_blocks_per_seq, block_size);
   const int32_t ms = max_splits_for(max_blocks_per_seq, block_size, split);
@@ -178,7 +199,14 @@ pa_status pa_decode(const void* q, int64_t q_tok_stride, const void* k_cache, co
   const bool out_bf16 = out_dtype == PA_BF16;
   const bool mfma = decode_uses_mfma(dtype, num_heads, num_kv_heads, head_dim) && q_tok_stride % 8 == 0 &&
                     aligned(q, 16) && aligned(k_cache, 16) && aligned(v_cache, 16) && aligned(out, 16);
-  if (mfma) {
+  if (mfma && decode_uses_stream(split_tokens, num_heads, num_kv_heads, head_dim, max_blocks_per_seq, block_size, batch)) {
+    const size_t need = pa::decode_stream_workspace_bytes(kStreamWorkers);
+    if (workspace_bytes < need) return PA_ERR_WORKSPACE;
+    if (!workspace || !aligned(workspace, 16)) return PA_ERR_NULL;
+    pa::launch_decode_stream(q, q_tok_stride, k_cache, v_cache, context_lens, block_table, max_blocks_per_seq, batch,
+                             num_heads, num_kv_heads, block_size, softmax_scale, out, out_bf16, kStreamWorkers,
+                             workspace, st);
+  } else if (mfma) {
     const int32_t split = split_tokens > 0 ? split_tokens
                                            : auto_split(batch, num_kv_heads, max_blocks_per_seq, block_size);
     const int32_t ms = max_splits_for(max_blocks_per_seq, block_size, split);

@@ -15,99 +15,13 @@
 // whatever the cache holds there (NaN included) cannot reach the output. The split/merge scheme is the
 // standard log-sum-exp combination; the pages do not describe the decode kernel's internals (they only name
 // the FlashAttention KV-cache call, "Nano-vLLM 架构详解" §3.2).
-#include "pa_launch.h"
+#include "pa_decode_tile.h"
 
 namespace pa {
 
-constexpr int kDecKeys = 32;       // keys per tile (two 16-key score tiles)
-constexpr int kVRow = 128 + 8;     // LDS row stride of the V tile, in bf16 elements (272 bytes)
 #ifndef PA_DECODE_WAVES
 #define PA_DECODE_WAVES 2
 #endif
-#ifndef PA_DECODE_NBUF
-#define PA_DECODE_NBUF 2
-#endif
-constexpr int kNBuf = PA_DECODE_NBUF;  // tiles whose loads are in flight per wave (software pipeline depth)
-
-template <bool kPow2>
-__device__ __forceinline__ int64_t slot_of_key(const int32_t* table, int key, int bs, int bs_shift) {
-  if (kPow2) return int64_t(table[key >> bs_shift]) * bs + (key & (bs - 1));
-  const int blk = key / bs;
-  return int64_t(table[blk]) * bs + (key - blk * bs);
-}
-
-// One tile of K and V rows in registers. k[tt][ks]: key base + 16tt + li, d 8lg + 32ks .. +7 (the A operand of the
-// score MFMA); v[it]: key base + 4it + lg, d 8li .. +7 (staged to LDS before use).
-struct KVTile {
-  u32x4 k[2][4];
-  u32x4 v[8];
-};
-
-// Byte offsets of this lane's pieces inside a tile, the same for every tile.
-struct LaneOffsets {
-  uint32_t k;  // li * row_bytes + 16 lg
-  uint32_t v;  // lg * row_bytes + 16 li
-};
-
-__device__ __forceinline__ u32x4 ld16_off(const char* base, uint32_t off) {
-  return *reinterpret_cast<const u32x4*>(base + off);
-}
-
-// Loads the tile of keys base .. base+31 (keys >= t1 read as zero).
-//
-// kAligned (block size a multiple of 32): the tile lies in one block, so its block id is read once as a
-// wave-uniform scalar and the tile is read through a raw buffer descriptor based at the tile's first row and
-// sized to its valid rows. Rows past the end fall outside the descriptor and the hardware returns zeros for
-// them without touching memory, so there is no branch per load and the number of loads in flight is the same
-// on every path. A tile wholly past the end gets a zero-sized descriptor (based at the first tile's block, so
-// the table entry read is always a real one).
-template <bool kAligned, bool kPow2>
-__device__ __forceinline__ void load_tile(KVTile& t, const char* __restrict__ kbase, const char* __restrict__ vbase,
-                                          const int32_t* __restrict__ table, int base, int t0, int t1, int bs,
-                                          int bs_shift, int64_t row_bytes, LaneOffsets lo, int lane) {
-  const u32x4 z = {0u, 0u, 0u, 0u};
-  const int lg = lane >> 4;
-  const int li = lane & 15;
-  if (kAligned) {
-    const int n = max(0, min(kDecKeys, t1 - base));  // valid rows of this tile
-    const int key0 = n > 0 ? base : t0;
-    const int blk = kPow2 ? (key0 >> bs_shift) : (key0 / bs);
-    const int phys = __builtin_amdgcn_readfirstlane(table[blk]);
-    const int64_t tile_off = (int64_t(phys) * bs + (key0 - blk * bs)) * row_bytes;
-    const int nbytes = __builtin_amdgcn_readfirstlane(int(n * row_bytes));
-    const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<char*>(kbase + tile_off), 0, nbytes, 0x00020000);
-    const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<char*>(vbase + tile_off), 0, nbytes, 0x00020000);
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
-      const int off = int(lo.k) + int(16 * tt * row_bytes);
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) t.k[tt][ks] = __builtin_amdgcn_raw_buffer_load_b128(kr, off + 64 * ks, 0, 0);
-    }
-#pragma unroll
-    for (int it = 0; it < 8; ++it)
-      t.v[it] = __builtin_amdgcn_raw_buffer_load_b128(vr, int(lo.v) + int(4 * it * row_bytes), 0, 0);
-  } else {
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
-      const int key = base + 16 * tt + li;
-      if (key < t1) {
-        const char* kp = kbase + slot_of_key<kPow2>(table, key, bs, bs_shift) * row_bytes + 16 * lg;
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) t.k[tt][ks] = ld16(kp + 64 * ks);
-      } else {
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) t.k[tt][ks] = z;
-      }
-    }
-#pragma unroll
-    for (int it = 0; it < 8; ++it) {
-      const int key = base + 4 * it + lg;
-      t.v[it] = key < t1 ? ld16(vbase + slot_of_key<kPow2>(table, key, bs, bs_shift) * row_bytes + 16 * li) : z;
-    }
-  }
-}
 
 template <bool kAligned, bool kPow2, int kHeadsPerWG>
 __global__ __launch_bounds__(64 * kHeadsPerWG) __attribute__((amdgpu_waves_per_eu(PA_DECODE_WAVES, PA_DECODE_WAVES))) void decode_mfma_kernel(
@@ -141,16 +55,9 @@ __global__ __launch_bounds__(64 * kHeadsPerWG) __attribute__((amdgpu_waves_per_e
   const char* vbase = reinterpret_cast<const char*>(v_cache + h * 128);
   const LaneOffsets lo = {uint32_t(li * row_bytes + 16 * lg), uint32_t(lg * row_bytes + 16 * li)};
 
-  // B operand of the score MFMA: lane holds Q[g = li][d = 8lg + 32ks .. +7]
   bf16x8 qb[4];
-  {
-    const u32x4 z = {0u, 0u, 0u, 0u};
-    const uint16_t* qp = q + int64_t(s) * q_stride + int64_t(h * G + li) * 128 + 8 * lg;
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) qb[ks] = as_bf16x8(li < G ? ld16(qp + 32 * ks) : z);
-  }
+  load_q(qb, q + int64_t(s) * q_stride + int64_t(h * G) * 128, G, lane);
 
-  // one V tile per wave; each wave only touches its own tile, and LDS accesses of one wave complete in order
   // then start the first tiles' loads (Q is loaded first so that waiting for a tile also covers Q)
   KVTile buf[kNBuf];
 #pragma unroll
@@ -158,18 +65,15 @@ __global__ __launch_bounds__(64 * kHeadsPerWG) __attribute__((amdgpu_waves_per_e
     load_tile<kAligned, kPow2>(buf[b], kbase, vbase, table, t0 + b * kDecKeys, t0, t1, bs, bs_shift, row_bytes,
                                lo, lane);
 
+  // one V tile per wave; each wave only touches its own tile, and LDS accesses of one wave complete in order
   __shared__ __attribute__((aligned(16))) uint16_t vt_all[kHeadsPerWG][kDecKeys * kVRow];
-  uint16_t* vt = vt_all[wave];
+  const VTileLane vl = v_tile_lane(vt_all[wave], lane);
 
   f32x4 o[8];
 #pragma unroll
   for (int mt = 0; mt < 8; ++mt) o[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m = -INFINITY;
   float lsum = 0.f;
-  // A operand rows of O^T: lane (li, lg) reads keys 4lg..4lg+3 and 16+4lg..16+4lg+3 at d = 16mt + li
-  const uint16_t* r0 = &vt[(4 * lg + (li >> 2)) * kVRow + 4 * (li & 3)];
-  const uint16_t* r1 = r0 + 16 * kVRow;
-  uint16_t* vw = &vt[lg * kVRow + 8 * li];  // this lane's V piece it goes to row 4it + lg
 
   for (int g0 = t0; g0 < t1; g0 += kNBuf * kDecKeys) {
 #pragma unroll
@@ -178,54 +82,12 @@ __global__ __launch_bounds__(64 * kHeadsPerWG) __attribute__((amdgpu_waves_per_e
       // aligned path): its loads return zeros without touching memory, its scores are -inf and it leaves
       // m, l and O unchanged. Unconditional steps keep the count of loads in flight the same on every path.
       const int base = g0 + b * kDecKeys;
-      {
-        KVTile& t = buf[b];
-        // V rows to LDS (after the previous tile's transposed reads, which precede them in this wave's order)
-#pragma unroll
-        for (int it = 0; it < 8; ++it) st16(vw + 4 * it * kVRow, t.v[it]);
-        // scores: sc[tt][i] is key base + 16tt + 4lg + i, query column g = li
-        f32x4 sc[2];
-#pragma unroll
-        for (int tt = 0; tt < 2; ++tt) {
-          sc[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int ks = 0; ks < 4; ++ks) sc[tt] = mfma16x16x32(as_bf16x8(t.k[tt][ks]), qb[ks], sc[tt]);
-        }
-        // the registers of this tile are free: start loading the tile kNBuf tiles ahead into them
-        load_tile<kAligned, kPow2>(t, kbase, vbase, table, base + kNBuf * kDecKeys, t0, t1, bs, bs_shift,
-                                   row_bytes, lo, lane);
-        float mx = -INFINITY;
-#pragma unroll
-        for (int tt = 0; tt < 2; ++tt) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int key = base + 16 * tt + 4 * lg + i;
-            const float v = key < t1 ? sc[tt][i] * scale_log2 : -INFINITY;
-            sc[tt][i] = v;
-            mx = fmaxf(mx, v);
-          }
-        }
-        mx = xgroup16_max(mx);
-        const float mn = fmaxf(m, mx);  // finite: the first tile holds at least one key
-        const float alpha = exp2f(m - mn);
-        m = mn;
-        float pv[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) pv[j] = exp2f(sc[j >> 2][j & 3] - mn);
-#pragma unroll
-        for (int mt = 0; mt < 8; ++mt) o[mt] *= alpha;
-        const u32x4 pw = {pack_weights_bf16x2(pv[0], pv[1]), pack_weights_bf16x2(pv[2], pv[3]),
-                          pack_weights_bf16x2(pv[4], pv[5]), pack_weights_bf16x2(pv[6], pv[7])};
-        lsum = lsum * alpha + ((sum_bf16x2(pw[0]) + sum_bf16x2(pw[1])) + (sum_bf16x2(pw[2]) + sum_bf16x2(pw[3])));
-        const bf16x8 pb = as_bf16x8(pw);
-#pragma unroll
-        for (int mt = 0; mt < 8; ++mt) {
-          const i16x4 a0 = lds_read_tr16(r0 + 16 * mt);
-          const i16x4 a1 = lds_read_tr16(r1 + 16 * mt);
-          const bf16x8 av = __builtin_bit_cast(bf16x8, __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7));
-          o[mt] = mfma16x16x32(av, pb, o[mt]);
-        }
-      }
+      f32x4 sc[2];
+      tile_scores(buf[b], qb, vl, sc);
+      // the registers of this tile are free: start loading the tile kNBuf tiles ahead into them
+      load_tile<kAligned, kPow2>(buf[b], kbase, vbase, table, base + kNBuf * kDecKeys, t0, t1, bs, bs_shift,
+                                 row_bytes, lo, lane);
+      tile_softmax_pv(sc, base, t1, scale_log2, lane, vl, o, m, lsum);
     }
   }
 

@@ -24,6 +24,13 @@ void launch_decode_mfma(const void* q, int64_t q_stride, const void* k_cache, co
                         int32_t Hq, int32_t Hkv, int32_t block_size, float scale, void* out, bool out_bf16,
                         int32_t split_tokens, int32_t max_splits, void* workspace, hipStream_t stream);
 
+size_t decode_stream_workspace_bytes(int32_t n_workers);
+
+void launch_decode_stream(const void* q, int64_t q_stride, const void* k_cache, const void* v_cache,
+                          const int32_t* ctx_lens, const int32_t* block_table, int32_t mbps, int32_t batch,
+                          int32_t Hq, int32_t Hkv, int32_t block_size, float scale, void* out, bool out_bf16,
+                          int32_t n_workers, void* workspace, hipStream_t stream);
+
 void launch_prefill_mfma(const void* q, int64_t q_stride, const void* k_cache, const void* v_cache,
                          const int32_t* cu_q, const int32_t* cu_k, const int32_t* block_table, int32_t mbps,
                          int32_t batch, int32_t max_seqlen_q, int32_t Hq, int32_t Hkv, int32_t block_size,

@@ -17,9 +17,10 @@
 // scores), so cache contents there cannot reach the output.
 //
 // Workgroup order: the flat grid is renumbered so that the workgroups the hardware sends to one XCD (every
-// eighth) get consecutive logical ids, and the logical order is (KV head, sequence, query tile from the last,
+// eighth) get consecutive logical ids, and the logical order is (KV head, query tile from the last, sequence,
 // query head in the group). The G query heads that share a KV head, and the query tiles of that head, then run
-// on one XCD and read the same K/V through its L2; the heaviest (last) tiles of each sequence start first.
+// on one XCD and read the same K/V through its L2; the last (heaviest, under the causal mask) query tiles of
+// all sequences start first, so the short tail of light tiles balances the finish.
 #include <type_traits>
 
 #include "pa_launch.h"
@@ -114,69 +115,78 @@ __device__ __forceinline__ void pf_scores(f32x16 (&sc)[kSub], const uint16_t* kt
   }
 }
 
-// Online softmax of one tile's scores (mask, running max, weights) and O^T += V^T P^T from the V tile in LDS.
-__device__ __forceinline__ void pf_softmax_pv(f32x16 (&sc)[kSub], f32x16 (&o)[4], float& m, float& lsum,
-                                              const uint16_t* vt, int va_off, int kb, bool need_mask, int my_pos,
-                                              int hh, float scale_log2) {
-  if (need_mask) {
+// Causal mask of one tile's scores (only called where some key of the tile is after some row of the wave).
+__device__ __forceinline__ void pf_mask(f32x16 (&sc)[kSub], int kb, int my_pos, int hh) {
 #pragma unroll
-    for (int sub = 0; sub < kSub; ++sub)
+  for (int sub = 0; sub < kSub; ++sub)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int key = kb + 32 * sub + 8 * (i >> 2) + 4 * hh + (i & 3);
-        if (key > my_pos) sc[sub][i] = -INFINITY;
-      }
-  }
+    for (int i = 0; i < 16; ++i) {
+      const int key = kb + 32 * sub + 8 * (i >> 2) + 4 * hh + (i & 3);
+      if (key > my_pos) sc[sub][i] = -INFINITY;
+    }
+}
+
+// Row max of one tile's scores, in scaled log2 units (-inf if all masked).
+__device__ __forceinline__ float pf_rowmax(const f32x16 (&sc)[kSub], float scale_log2) {
   float mx = -INFINITY;
 #pragma unroll
   for (int sub = 0; sub < kSub; ++sub)
 #pragma unroll
     for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sc[sub][i]);
-  mx = xhalf_max(mx) * scale_log2;  // the tile's row max in scaled log2 units (-inf if all masked)
-  // The reference max only moves when the row max would exceed it by more than the slack; until then the
-  // weights exp2(s - m) stay below 2^8 and O, l need no rescaling. The result O / l does not depend on m.
-  if (__any(mx > m + kRescaleSlack)) {
-    const float mn = fmaxf(m, mx);
-    const float alpha = __builtin_amdgcn_exp2f(m - mn);  // 0 on the first tile (m = -inf)
-    m = mn;
-    lsum *= alpha;
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) o[mt] *= alpha;
-  }
-  // weights in fp16 (round to nearest); the row sum is taken over the rounded weights that enter the PV
-  // product, so the weights the output averages with sum to one
+  return xhalf_max(mx) * scale_log2;
+}
+
+// Weights of one tile (fp16, round to nearest; the row sum is taken over the rounded weights that enter the PV
+// product, so the weights the output averages with sum to one) and O^T += V^T P^T from the V tile in LDS.
+// Lane group g4 = lane / 16 (half hh = g4 / 2, d offset 16 (g4 % 2)); for k-step kk the lane's slots 0..3 are
+// keys 16 kk + 4 hh + 0..3 and slots 4..7 keys 16 kk + 8 + 4 hh + 0..3.
+__device__ __forceinline__ void pf_weights_pv(f32x16 (&sc)[kSub], f32x16 (&o)[4], float m, float& lsum,
+                                              const uint16_t* vt, int va_off, float scale_log2) {
   float psum = 0.f;
-  f16x8 pb[2 * kSub];
 #pragma unroll
   for (int sub = 0; sub < kSub; ++sub) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) sc[sub][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[sub][i], scale_log2, -m));
-#pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
-      const u32x4 pw = {pack_f16x2(sc[sub][8 * kk + 0], sc[sub][8 * kk + 1]),
-                        pack_f16x2(sc[sub][8 * kk + 2], sc[sub][8 * kk + 3]),
-                        pack_f16x2(sc[sub][8 * kk + 4], sc[sub][8 * kk + 5]),
-                        pack_f16x2(sc[sub][8 * kk + 6], sc[sub][8 * kk + 7])};
+      float p[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[sub][8 * kk + i], scale_log2, -m));
+      const u32x4 pw = {pack_f16x2(p[0], p[1]), pack_f16x2(p[2], p[3]), pack_f16x2(p[4], p[5]),
+                        pack_f16x2(p[6], p[7])};
       psum = add_f16x2(pw[3], add_f16x2(pw[2], add_f16x2(pw[1], add_f16x2(pw[0], psum))));
-      pb[2 * sub + kk] = as_f16x8(pw);
-    }
-  }
-  lsum += psum;
-  // O^T += V^T P^T. Lane group g4 = lane / 16 (half hh = g4 / 2, d offset 16 (g4 % 2)); for k-step kk the lane's
-  // slots 0..3 are keys 16 kk + 4 hh + 0..3 and slots 4..7 keys 16 kk + 8 + 4 hh + 0..3.
-#pragma unroll
-  for (int sub = 0; sub < kSub; ++sub) {
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
+      const f16x8 pb = as_f16x8(pw);
       const uint16_t* vr = vt + va_off + (32 * sub + 16 * kk) * kVRow;
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
         const i16x4 a0 = lds_read_tr16(vr + 32 * mt);
         const i16x4 a1 = lds_read_tr16(vr + 8 * kVRow + 32 * mt);
         const f16x8 av = __builtin_bit_cast(f16x8, __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7));
-        o[mt] = mfma32x32x16_f16(av, pb[2 * sub + kk], o[mt]);
+        o[mt] = mfma32x32x16_f16(av, pb, o[mt]);
       }
     }
+  }
+  lsum += psum;
+}
+
+// Scheduling hints (instruction groups in issue order) for the two long blocks of a step.
+// Mask bits: 0x2 VALU, 0x8 MFMA, 0x20 VMEM read, 0x100 DS read, 0x200 DS write.
+__device__ __forceinline__ void pf_sched_scores() {
+  __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+  }
+}
+__device__ __forceinline__ void pf_sched_weights_pv() {
+  __builtin_amdgcn_sched_group_barrier(0x002, 24, 0);
+  __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
+    __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
   }
 }
 
@@ -193,10 +203,10 @@ __global__ __launch_bounds__(kPreThreads) __attribute__((amdgpu_waves_per_eu(2, 
   const int G = Hq / Hkv;
   const int gi = logical % G;
   int rest = logical / G;
-  const int qtile = n_qtiles - 1 - rest % n_qtiles;
-  rest /= n_qtiles;
   const int s = rest % batch;
-  const int kvh = rest / batch;
+  rest /= batch;
+  const int qtile = n_qtiles - 1 - rest % n_qtiles;
+  const int kvh = rest / n_qtiles;
   const int h = kvh * G + gi;
 
   const int q0 = cu_q[s];
@@ -262,7 +272,7 @@ __global__ __launch_bounds__(kPreThreads) __attribute__((amdgpu_waves_per_eu(2, 
   pf_lstore_k(kst, kt[1], tid);
   __syncthreads();
   f32x16 sa[kSub], sb[kSub];
-  if (wave_tiles > 0) pf_scores(sa, kt[0], ka_off, qb);
+  pf_scores(sa, kt[0], ka_off, qb);
   __syncthreads();  // K tile 0 has been read by every wave before iteration 0 replaces it
 
   auto step = [&](int j, f32x16 (&cur)[kSub], f32x16 (&nxt)[kSub], auto par) {
@@ -271,12 +281,30 @@ __global__ __launch_bounds__(kPreThreads) __attribute__((amdgpu_waves_per_eu(2, 
     // K tile j+2 and V tile j+1 start loading (past the end they read as zero and touch no memory)
     pf_gload1<kAligned, kPow2>(kst, kbase, table, kb + 2 * kPreKeys, k_len, bs, bs_shift, row_bytes, tid);
     pf_gload1<kAligned, kPow2>(vst, vbase, table, kb + kPreKeys, k_len, bs, bs_shift, row_bytes, tid);
-    if (j + 1 < wave_tiles) pf_scores(nxt, kt[1 - P], ka_off, qb);
-    if (j < wave_tiles)
-      pf_softmax_pv(cur, o, m, lsum, vt[P], va_off, kb, kb + kPreKeys - 1 > past + wave_row0, my_pos, hh,
-                    scale_log2);
-    pf_lstore_k(kst, kt[P], tid);      // K tile j was last read in the previous step
-    pf_lstore_v(vst, vt[1 - P], tid);  // V tile j-1 was last read in the previous step
+    if (j < wave_tiles) {
+      if (kb + kPreKeys - 1 > past + wave_row0) pf_mask(cur, kb, my_pos, hh);
+      // tile j+1's scores on the matrix cores while tile j's row max runs on the vector ALUs
+      pf_scores(nxt, kt[1 - P], ka_off, qb);
+      const float mx = pf_rowmax(cur, scale_log2);
+      pf_sched_scores();
+      // The reference max only moves when the row max would exceed it by more than the slack; until then the
+      // weights exp2(s - m) stay below 2^8 and O, l need no rescaling. The result O / l does not depend on m.
+      if (__any(mx > m + kRescaleSlack)) {
+        const float mn = fmaxf(m, mx);
+        const float alpha = __builtin_amdgcn_exp2f(m - mn);  // 0 on the first tile (m = -inf)
+        m = mn;
+        lsum *= alpha;
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) o[mt] *= alpha;
+      }
+      pf_weights_pv(cur, o, m, lsum, vt[P], va_off, scale_log2);
+      pf_lstore_k(kst, kt[P], tid);      // K tile j was last read in the previous step
+      pf_lstore_v(vst, vt[1 - P], tid);  // V tile j-1 was last read in the previous step
+      pf_sched_weights_pv();
+    } else {
+      pf_lstore_k(kst, kt[P], tid);
+      pf_lstore_v(vst, vt[1 - P], tid);
+    }
     __syncthreads();
   };
   for (int j = 0; j < n_tiles; j += 2) {

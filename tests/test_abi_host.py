@@ -109,10 +109,20 @@ def test_decode_workspace_query():
     assert pa.decode_workspace_bytes(64, 16, 8, 128, 16, 256, 4096) == 0
     # B * Hq * splits * (D + 2) floats
     assert pa.decode_workspace_bytes(64, 16, 8, 128, 16, 256, 256) == 64 * 16 * 16 * (128 + 2) * 4
-    s = pa.decode_split_tokens(256, 64, 8, 128, 128, 256)
+    s = pa.decode_split_tokens(256, 64, 8, 128, 128, 16)
     assert s % 32 == 0 and 256 <= s <= 4096
-    assert pa.decode_workspace_bytes(256, 64, 8, 128, 128, 256, 0) == \
-        pa.decode_workspace_bytes(256, 64, 8, 128, 128, 256, s)
+    # split_tokens = 0 with a block size that is not a multiple of 32: the library's fixed split
+    assert pa.decode_workspace_bytes(256, 64, 8, 128, 128, 16, 0) == \
+        pa.decode_workspace_bytes(256, 64, 8, 128, 128, 16, s)
+    # split_tokens = 0, D = 128, G <= 16, block size 256: balanced decode, two partial slots of
+    # m[16], l[16], O[16][128] floats per worker, whatever the batch
+    slot = (16 + 16 + 16 * 128) * 4
+    ws = pa.decode_workspace_bytes(256, 64, 8, 128, 128, 256, 0)
+    assert ws % (2 * slot) == 0 and ws // (2 * slot) >= 1024
+    assert pa.decode_workspace_bytes(1, 64, 8, 128, 128, 256, 0) == ws
+    # G = 32 query heads per KV head: fixed split
+    assert pa.decode_workspace_bytes(4, 32, 1, 128, 128, 256, 0) == \
+        pa.decode_workspace_bytes(4, 32, 1, 128, 128, 256, pa.decode_split_tokens(4, 32, 1, 128, 128, 256))
 
 
 def test_binding_checks_layouts_on_the_host():

@@ -142,6 +142,11 @@ DECODE_CASES = [
     (32, 1, 128, 16, "bf16", [40, 90], 0),
     (8, 2, 128, 16, "f32", [70, 33], 0),
     (4, 2, 64, 16, "bf16", [70, 33], 0),
+    # balanced decode (split_tokens = 0, D = 128, block size a multiple of 32): G = 16 with 32-key blocks; many
+    # short mixed lengths; one long sequence whose pairs are cut across more than 64 worker slices
+    (16, 1, 128, 32, "bf16", [1, 31, 32, 33, 5000], 0),
+    (32, 8, 128, 64, "bf16", [int(x) for x in np.random.default_rng(7).integers(1, 600, 300)], 0),
+    (8, 8, 128, 256, "bf16", [20000], 0),
 ]
 
 
