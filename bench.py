@@ -1,7 +1,8 @@
 """Benchmark of the paged-KV attention step on one MI355X.
 
 One step = one pass of the whole path over one batch: device-side metadata (slots, prefix sums), store_kvcache
-of the new tokens, then attention over the paged cache (decode: split pass + merge pass; prefill: one pass).
+of the new tokens, then attention over the paged cache (decode: balanced pass + merge of cut sequences;
+prefill: one pass).
 
 Main line: the decode workload with Qwen3-0.6B attention shape (64 sequences, 16 query / 8 KV heads, head_dim
 128, bf16, block_size 256, contexts U[128, 4096]). Consecutive steps use different per-layer cache pools (the
@@ -67,6 +68,13 @@ def algorithmic_work(wl, step, out_bytes: int):
 # ---------------------------------------------------------------------------------------------- GPU timing
 
 
+# Sources of the attention kernels each workload kind runs, and the kernels of one attention call: a traffic
+# summary taken on other sources is stale and not reported.
+ATTN_SOURCES = {"decode": ("pa_decode_stream.hip", "pa_decode_tile.h", "pa_common.h", "pa_api.hip"),
+                "prefill": ("pa_prefill.hip", "pa_common.h")}
+ATTN_KERNELS = {"decode": ("decode_stream_kernel", "decode_stream_merge_kernel"), "prefill": ("prefill_mfma_kernel",)}
+
+
 def _src_sha(*names) -> str:
     h = hashlib.sha256()
     for n in names:
@@ -85,6 +93,71 @@ def _traffic(profile_name: str, sha: str):
     if d.get("source_sha") != sha:
         return None
     return d.get("hbm_bytes_per_launch")
+
+
+def write_traffic_summary(workload: str, fetch_csv: str, write_csv: str) -> dict:
+    """profiles/<workload>_hbm_traffic.json from two rocprofv3 --pmc runs of this script with --calibrate-copy
+    (one with FETCH_SIZE, one with WRITE_SIZE, counter values in KiB per dispatch). Each counter is scaled by
+    known / measured on the plain copy kernel of the same run (torch.mul over 1 GiB of fp16: reads 1 GiB, writes
+    1 GiB); HBM bytes per launch = sum over the attention call's kernels of the scaled means."""
+    import collections
+    import csv
+
+    from workloads import make_config
+
+    kind = make_config(workload, fill=False).steps[-1].kind
+
+    def load(path):
+        agg = collections.defaultdict(list)
+        with open(path, newline="") as f:
+            for r in csv.DictReader(f):
+                agg[r["Kernel_Name"]].append(float(r["Counter_Value"]))
+        return agg
+
+    fetch, write = load(fetch_csv), load(write_csv)
+
+    def mean(agg, part):
+        keys = [k for k in agg if part in k]
+        if not keys:
+            raise SystemExit(f"no dispatch of a kernel named like {part!r} in the counter file")
+        vals = [v for k in keys for v in agg[k]]
+        return sum(vals) / len(vals), len(vals)
+
+    known_kib = (1 << 30) / 1024.0
+    copy_f, _ = mean(fetch, "vectorized_elementwise_kernel")
+    copy_w, _ = mean(write, "vectorized_elementwise_kernel")
+    fscale, wscale = known_kib / copy_f, known_kib / copy_w
+    per, total = {}, 0.0
+    for kn in ATTN_KERNELS[kind]:
+        fk, n = mean(fetch, kn)
+        wk, _ = mean(write, kn)
+        b = (fk * fscale + wk * wscale) * 1024
+        per[kn] = {"FETCH_SIZE_KiB": round(fk, 1), "WRITE_SIZE_KiB": round(wk, 1), "hbm_bytes": int(b),
+                   "dispatches": n}
+        total += b
+    out = {
+        "workload": workload,
+        "what": "HBM bytes per launch of the attention call from rocprofv3 FETCH_SIZE and WRITE_SIZE (KiB per "
+                "dispatch, mean over the profiled dispatches), each scaled by known / measured of the same counter "
+                "on a plain copy kernel (torch.mul over 1 GiB of fp16: reads 1 GiB, writes 1 GiB)",
+        "commands": [f"cd /tmp && rocprofv3 --pmc {c} -d gpurun_out/pmc_{c}_{workload} -o pmc --output-format csv "
+                     f"-- python /root/repo/bench.py --only {workload} --no-cpu-baseline --steps 5 --warmup 2 "
+                     f"--calibrate-copy" for c in ("FETCH_SIZE", "WRITE_SIZE")]
+                    + [f"python bench.py --only {workload} --traffic-summary "
+                       f"gpurun_out/pmc_FETCH_SIZE_{workload}/pmc_counter_collection.csv "
+                       f"gpurun_out/pmc_WRITE_SIZE_{workload}/pmc_counter_collection.csv"],
+        "copy_kernel": {"FETCH_SIZE_KiB": round(copy_f, 1), "WRITE_SIZE_KiB": round(copy_w, 1),
+                        "known_read_KiB": known_kib, "known_write_KiB": known_kib,
+                        "fetch_scale": round(fscale, 4), "write_scale": round(wscale, 4)},
+        "kernels": per,
+        "hbm_bytes_per_launch": int(total),
+        "source_files": list(ATTN_SOURCES[kind]),
+        "source_sha": _src_sha(*ATTN_SOURCES[kind]),
+    }
+    with open(os.path.join(ROOT, "profiles", f"{workload}_hbm_traffic.json"), "w", encoding="utf-8") as f:
+        json.dump(out, f, indent=1)
+        f.write("\n")
+    return out
 
 
 class GpuWorkload:
@@ -264,9 +337,17 @@ def main() -> int:
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for the CPU baseline")
+    ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"), default=None,
+                    help="write the HBM traffic summary of --only's workload from two rocprofv3 counter files "
+                         "(no GPU needed) and exit")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 1 GiB copy kernel (reference for the HBM byte counters)")
     args = ap.parse_args()
+    if args.traffic_summary:
+        if not args.only:
+            ap.error("--traffic-summary needs --only WORKLOAD")
+        print(json.dumps(write_traffic_summary(args.only, *args.traffic_summary), indent=1))
+        return 0
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the attention step runs "
               "on one GPU's share and has no cross-GPU exchange)", file=sys.stderr)
@@ -304,13 +385,13 @@ def main() -> int:
     t = main["timing"]
     work = main["work"]
     is_dec = main["kind"] == "decode"
-    sha = _src_sha("pa_decode.hip", "pa_common.h") if is_dec else _src_sha("pa_prefill.hip", "pa_common.h")
+    sha = _src_sha(*ATTN_SOURCES[main["kind"]])
     traffic = _traffic(f"{main_name}_hbm_traffic.json", sha)
     if is_dec:
         value = main["step_GBps"]
         roof = {"bound": "hbm", "achieved": round(main["attn_GBps"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(main["attn_frac_hbm"], 4), "traffic": traffic,
-                "kernel": "pa_decode (decode_mfma_kernel + decode_reduce_kernel)",
+                "kernel": "pa_decode (" + " + ".join(ATTN_KERNELS["decode"]) + ")",
                 "bytes_per_launch": work["attn_bytes"], "launch_ms": round(t["attn_ms"], 5)}
         unit = "GB/s"
     else:
@@ -329,7 +410,7 @@ def main() -> int:
                    "num_kv_heads": wl.num_kv_heads, "head_dim": wl.head_dim, "block_size": wl.block_size,
                    "sum_context": work["sum_k"], "new_tokens": work["tokens"], "seed": wl.seed,
                    "out_dtype": args.out_dtype, "layers_cycled": args.layers,
-                   "step": "metadata + store_kvcache + " + ("decode (split + merge)" if is_dec else "prefill")},
+                   "step": "metadata + store_kvcache + " + ("decode (balanced pass + merge)" if is_dec else "prefill")},
         "breakdown_ms": {"metadata": round(t["meta_ms"], 5), "store": round(t["store_ms"], 5),
                          "attention": round(t["attn_ms"], 5), "attention_median": round(t["attn_ms_median"], 5),
                          "events_step": round(t["step_ms"], 5)},
