@@ -38,10 +38,11 @@ bool decode_uses_mfma(pa_dtype dtype, int32_t Hq, int32_t Hkv, int32_t D) {
   return dtype == PA_BF16 && D == 128 && Hq / Hkv <= 16;
 }
 
-// Workers of the balanced decode (split_tokens == 0): two rounds of two waves per SIMD of the 256 CUs (measured
-// faster than one round on long contexts, equal on short ones).
+// Workers of the balanced decode (split_tokens == 0), one wave each: one and a half rounds of the 2048 that fit
+// at once (two waves per SIMD of the 256 CUs). Measured fastest of 2048 to 8192 on both short mixed and long
+// contexts: later workers fill the slots of early finishers, and slices stay long.
 #ifndef PA_STREAM_WORKERS
-#define PA_STREAM_WORKERS 4096
+#define PA_STREAM_WORKERS 3072
 #endif
 constexpr int32_t kStreamWorkers = PA_STREAM_WORKERS;
 

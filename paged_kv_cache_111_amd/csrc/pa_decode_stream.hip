@@ -60,6 +60,48 @@ __device__ __forceinline__ void stream_prefix(const int32_t* __restrict__ ctx_le
   __syncthreads();
 }
 
+// Position of a 32-key tile in the (KV head, sequence, key) order: KV head h, sequence s, first key t of the
+// tile, the sequence's length L and its length padded to 32 (all wave-uniform).
+struct StreamCursor {
+  int h, s, t, L, Lp;
+};
+
+// Steps to the next tile: the next 32 keys of the pair, or key 0 of the next pair with keys (the next sequence,
+// then the next KV head). Callers step only while another tile of the slice follows, so a pair with keys lies
+// ahead; the scan over zero-length sequences is bounded by the batch all the same.
+__device__ __forceinline__ void cursor_next(StreamCursor& c, const int32_t* lens, int batch) {
+  c.t += kDecKeys;
+  if (c.t >= c.Lp) {
+    c.t = 0;
+    for (int k = 0; k < batch; ++k) {
+      if (++c.s == batch) {
+        c.s = 0;
+        ++c.h;
+      }
+      c.L = __builtin_amdgcn_readfirstlane(lens[c.s]);
+      c.Lp = (c.L + 31) & ~31;
+      if (c.Lp > 0) break;
+    }
+  }
+}
+
+// Q^T of a (sequence, KV head) pair as the score MFMA's B operand (lane: Q[g = li][d = 8lg + 32ks .. +7]),
+// read through a buffer descriptor sized to the G rows so lanes li >= G get zeros with no branch.
+__device__ __forceinline__ void load_q_rsrc(bf16x8 (&qb)[4], const uint16_t* qrow0, int G, int lane) {
+  const int lg = lane >> 4;
+  const int li = lane & 15;
+  const __amdgpu_buffer_rsrc_t r =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(qrow0), 0, G * 256, 0x00020000);
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) qb[ks] = as_bf16x8(__builtin_amdgcn_raw_buffer_load_b128(r, li * 256 + 16 * lg + 64 * ks, 0, 0));
+}
+
+// A worker's slice is a run of whole 32-key tiles (slice ends and padded lengths are multiples of 32), walked as
+// one stream: the loads of tile i + NBUF (and the Q of tile i + 1's pair) are issued while tile i is computed,
+// whether or not the tiles belong to the same (sequence, KV head) pair, so the loads stay in flight across pair
+// boundaries. When the tile ends a piece (the end of its pair, or of the slice) the piece is finished: a pair
+// held whole is normalised into the output; a cut pair leaves (m, l, O) in partial slot 0 (the slice's first
+// piece) or 1 (its last).
 template <bool kPow2>
 __global__ __launch_bounds__(64 * kStreamWaves) __attribute__((amdgpu_waves_per_eu(2, 2))) void decode_stream_kernel(
     const uint16_t* __restrict__ q, int64_t q_stride, const uint16_t* __restrict__ k_cache,
@@ -78,8 +120,10 @@ __global__ __launch_bounds__(64 * kStreamWaves) __attribute__((amdgpu_waves_per_
   const int64_t chunk = ((total + n_workers - 1) / n_workers + 31) & ~int64_t(31);
   const int wave = __builtin_amdgcn_readfirstlane(int(threadIdx.x >> 6));
   const int wid = int(blockIdx.x) * kStreamWaves + wave;
-  int64_t u = int64_t(wid) * chunk;
-  const int64_t u_end = min(total, u + chunk);
+  const int64_t u0 = int64_t(wid) * chunk;
+  const int64_t u1 = min(total, u0 + chunk);
+  if (u0 >= u1) return;
+  const int n_tiles = int((u1 - u0) / kDecKeys);
 
   const int G = Hq / Hkv;
   const int lane = threadIdx.x & 63;
@@ -88,85 +132,112 @@ __global__ __launch_bounds__(64 * kStreamWaves) __attribute__((amdgpu_waves_per_
   const int64_t row_bytes = int64_t(Hkv) * 256;
   const LaneOffsets lo = {uint32_t(li * row_bytes + 16 * lg), uint32_t(lg * row_bytes + 16 * li)};
   const VTileLane vl = v_tile_lane(vt_all[wave], lane);
-  int slot = 0;  // 0 for the slice's first pair, 1 for its last
 
-  while (u < u_end) {
-    const int h = int(u / Tp);
-    const int r = int(u - int64_t(h) * Tp);
-    int a = 0, b = batch;  // the pair's sequence: cum[a] <= r < cum[b]
+  StreamCursor cc;  // the tile being computed
+  {
+    const int h = int(u0 / Tp);
+    const int r = int(u0 - int64_t(h) * Tp);
+    int a = 0, b = batch;  // cum[a] <= r < cum[a + 1]
     while (b - a > 1) {
       const int mid = (a + b) >> 1;
       if (cum[mid] <= r) a = mid; else b = mid;
     }
-    // (LDS values are the same in every lane; readfirstlane tells the compiler they are wave-uniform)
-    const int s = __builtin_amdgcn_readfirstlane(a);
-    const int t0 = __builtin_amdgcn_readfirstlane(r - cum[s]);  // first key of this piece of the pair
-    const int Lp = __builtin_amdgcn_readfirstlane(cum[s + 1] - cum[s]);
-    const int L = __builtin_amdgcn_readfirstlane(lens[s]);
-    const int seg = int(min(int64_t(Lp - t0), u_end - u));
-    const int t1 = min(L, t0 + seg);                  // real keys of the piece end here
-    const bool whole = t0 == 0 && seg == Lp;
+    cc.h = h;
+    cc.s = __builtin_amdgcn_readfirstlane(a);
+    cc.t = __builtin_amdgcn_readfirstlane(r - cum[cc.s]);
+    cc.L = __builtin_amdgcn_readfirstlane(lens[cc.s]);
+    cc.Lp = (cc.L + 31) & ~31;
+  }
+  StreamCursor lc = cc;  // the next tile to load
 
-    f32x4 o[8];
+  auto qrow = [&](const StreamCursor& c) { return q + int64_t(c.s) * q_stride + int64_t(c.h * G) * 128; };
+  // Loads the tile at lc; a tile index past the slice gets a zero-sized descriptor at lc's (real) tile.
+  auto issue = [&](KVTile& t, bool real) {
+    load_tile<true, kPow2>(t, reinterpret_cast<const char*>(k_cache + lc.h * 128),
+                           reinterpret_cast<const char*>(v_cache + lc.h * 128), block_table + int64_t(lc.s) * mbps,
+                           lc.t, lc.t, real ? lc.L : lc.t, bs, bs_shift, row_bytes, lo, lane);
+  };
+
+  bf16x8 qb[4];
+  load_q_rsrc(qb, qrow(cc), G, lane);
+  KVTile buf[kStreamNBuf];
 #pragma unroll
-    for (int mt = 0; mt < 8; ++mt) o[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float m = -INFINITY;
-    float lsum = 0.f;
-    if (t0 < L) {  // the piece holds at least one real key (else it only covers padding)
-      const int32_t* table = block_table + int64_t(s) * mbps;
-      const char* kbase = reinterpret_cast<const char*>(k_cache + h * 128);
-      const char* vbase = reinterpret_cast<const char*>(v_cache + h * 128);
-      bf16x8 qb[4];
-      load_q(qb, q + int64_t(s) * q_stride + int64_t(h * G) * 128, G, lane);
-      KVTile buf[kStreamNBuf];
+  for (int bb = 0; bb < kStreamNBuf; ++bb) {
+    issue(buf[bb], bb < n_tiles);
+    if (bb + 1 < n_tiles) cursor_next(lc, lens, batch);
+  }
+
+  f32x4 o[8];
 #pragma unroll
-      for (int bb = 0; bb < kStreamNBuf; ++bb)
-        load_tile<true, kPow2>(buf[bb], kbase, vbase, table, t0 + bb * kDecKeys, t0, t1, bs, bs_shift, row_bytes,
-                               lo, lane);
-      for (int g0 = t0; g0 < t1; g0 += kStreamNBuf * kDecKeys) {
+  for (int mt = 0; mt < 8; ++mt) o[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m = -INFINITY;
+  float lsum = 0.f;
+  int slot = 0;
+  bool from_start = cc.t == 0;  // the current piece starts at its pair's first key
+
+  // Every pass of the body issues the same loads in the same order (past the slice they are zero-sized), and
+  // only the compute is skipped there, so the wait counts before each tile are the same on every path.
+  for (int i0 = 0; i0 < n_tiles; i0 += kStreamNBuf) {
 #pragma unroll
-        for (int bb = 0; bb < kStreamNBuf; ++bb) {
-          const int base = g0 + bb * kDecKeys;
-          f32x4 sc[2];
-          tile_scores(buf[bb], qb, vl, sc);
-          load_tile<true, kPow2>(buf[bb], kbase, vbase, table, base + kStreamNBuf * kDecKeys, t0, t1, bs,
-                                 bs_shift, row_bytes, lo, lane);
-          tile_softmax_pv(sc, base, t1, scale_log2, lane, vl, o, m, lsum);
-        }
-      }
-    }
-    lsum = xgroup16_sum(lsum);
-    if (li < G) {
-      // o[mt][i] is O^T[d = 16mt + 4lg + i][g = li]
-      if (whole) {
-        const float inv = 1.f / lsum;
-        const int64_t ob = (int64_t(s) * Hq + h * G + li) * 128 + 4 * lg;
-        if (out_bf16) {
-          uint16_t* op = static_cast<uint16_t*>(out) + ob;
+    for (int bb = 0; bb < kStreamNBuf; ++bb) {
+      const int i = i0 + bb;
+      const bool active = i < n_tiles;
+      const bool pair_end = cc.t + kDecKeys >= cc.Lp;
+      const bool piece_end = active && (pair_end || i + 1 == n_tiles);
+      StreamCursor nc = cc;
+      if (i + 1 < n_tiles) cursor_next(nc, lens, batch);
+
+      f32x4 sc[2];
+      if (active) tile_scores(buf[bb], qb, vl, sc);
+      bf16x8 qn[4];
+      load_q_rsrc(qn, qrow(nc), G, lane);
+      const int j = i + kStreamNBuf;
+      issue(buf[bb], j < n_tiles);
+      if (j + 1 < n_tiles) cursor_next(lc, lens, batch);
+      if (active) tile_softmax_pv(sc, cc.t, cc.L, scale_log2, lane, vl, o, m, lsum);
+
+      if (piece_end) {
+        const float ls = xgroup16_sum(lsum);
+        if (li < G) {
+          // o[mt][i] is O^T[d = 16mt + 4lg + i][g = li]
+          if (from_start && pair_end) {
+            const float inv = 1.f / ls;
+            const int64_t ob = (int64_t(cc.s) * Hq + cc.h * G + li) * 128 + 4 * lg;
+            if (out_bf16) {
+              uint16_t* op = static_cast<uint16_t*>(out) + ob;
 #pragma unroll
-          for (int mt = 0; mt < 8; ++mt) {
-            const u32x2 w = {pack_bf16x2(o[mt][0] * inv, o[mt][1] * inv),
-                             pack_bf16x2(o[mt][2] * inv, o[mt][3] * inv)};
-            *reinterpret_cast<u32x2*>(op + 16 * mt) = w;
+              for (int mt = 0; mt < 8; ++mt) {
+                const u32x2 w = {pack_bf16x2(o[mt][0] * inv, o[mt][1] * inv),
+                                 pack_bf16x2(o[mt][2] * inv, o[mt][3] * inv)};
+                *reinterpret_cast<u32x2*>(op + 16 * mt) = w;
+              }
+            } else {
+              float* op = static_cast<float*>(out) + ob;
+#pragma unroll
+              for (int mt = 0; mt < 8; ++mt) *reinterpret_cast<f32x4*>(op + 16 * mt) = o[mt] * inv;
+            }
+          } else {
+            float* pp = part + (int64_t(wid) * 2 + slot) * kSlotFloats;
+            if (lg == 0) {
+              pp[li] = m;
+              pp[16 + li] = ls;
+            }
+            float* po = pp + 32 + li * 128 + 4 * lg;
+#pragma unroll
+            for (int mt = 0; mt < 8; ++mt) *reinterpret_cast<f32x4*>(po + 16 * mt) = o[mt];
           }
-        } else {
-          float* op = static_cast<float*>(out) + ob;
-#pragma unroll
-          for (int mt = 0; mt < 8; ++mt) *reinterpret_cast<f32x4*>(op + 16 * mt) = o[mt] * inv;
         }
-      } else {
-        float* pp = part + (int64_t(wid) * 2 + slot) * kSlotFloats;
-        if (lg == 0) {
-          pp[li] = m;
-          pp[16 + li] = lsum;
-        }
-        float* po = pp + 32 + li * 128 + 4 * lg;
 #pragma unroll
-        for (int mt = 0; mt < 8; ++mt) *reinterpret_cast<f32x4*>(po + 16 * mt) = o[mt];
+        for (int mt = 0; mt < 8; ++mt) o[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        m = -INFINITY;
+        lsum = 0.f;
+        slot = 1;
+        from_start = true;
       }
+      cc = nc;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) qb[ks] = qn[ks];
     }
-    slot = 1;
-    u += seg;
   }
 }
 
@@ -200,6 +271,7 @@ __global__ __launch_bounds__(64) void decode_stream_merge_kernel(const int32_t* 
   const int64_t chunk = ((total + n_workers - 1) / n_workers + 31) & ~int64_t(31);
   const int64_t a = int64_t(h) * all + before;
   const int64_t b = a + ((ctx_lens[s] + 31) & ~31);
+  if (b == a) return;  // no keys (lengths are documented >= 1)
   const int w0 = int(a / chunk);
   const int w1 = int((b - 1) / chunk);
   if (w0 == w1) return;
