@@ -36,4 +36,5 @@ void launch_prefill_mfma(const void* q, int64_t q_stride, const void* k_cache, c
                          int32_t batch, int32_t max_seqlen_q, int32_t Hq, int32_t Hkv, int32_t block_size,
                          float scale, void* out, bool out_bf16, hipStream_t stream);
 
+
 }  // namespace pa

@@ -121,6 +121,10 @@ PREFILL_CASES = [
     (8, 2, 128, 16, "f32", [70, 33], [20, 0]),
     (4, 4, 16, 4, "f32", [9, 13], [0, 5]),
     (32, 8, 128, 256, "bf16", [2048], [0]),
+    # two query heads per KV head with a block size that is not a power of two (tiles gathered key by key);
+    # 64-key blocks with one-key sequences and a chunk that starts inside a block
+    (8, 4, 128, 24, "bf16", [100, 61, 130], [50, 0, 129]),
+    (16, 8, 128, 64, "bf16", [500, 64, 65, 1], [436, 0, 1, 0]),
 ]
 
 
