@@ -8,8 +8,9 @@
 //                                           converted to fp16 when staged), B = P^T (fp16) kept in the
 //                                           registers the score MFMA left the scores in
 // With scores transposed, each lane owns one query column; its keys are split over the two wave halves, which
-// exchange the row max only when a tile moves the running reference max, and the row sum once at the end. The key -> k-slot assignment of the second product follows the score layout
-// (lane half hh holds keys 8j + 4hh .. +3), so P^T needs no data movement.
+// exchange the row max only when a tile moves the running reference max, and the row sum once at the end.
+// The key -> k-slot assignment of the second product follows the score layout (lane half hh holds keys
+// 8j + 4hh .. +3), so P^T needs no data movement.
 //
 // Causality follows absolute positions: the q_len new rows of a sequence with k_len keys sit at positions
 // k_len - q_len .. k_len - 1 (a chunk continues after the cached prefix, "Nano-vLLM 源码逐行解析 第2篇",

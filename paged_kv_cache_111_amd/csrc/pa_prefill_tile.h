@@ -6,8 +6,9 @@
 //                                           converted to fp16 when staged), B = P^T (fp16) kept in the
 //                                           registers the score MFMA left the scores in
 // With scores transposed, each lane owns one query column; its keys are split over the two wave halves, which
-// exchange the row max only when a tile moves the running reference max, and the row sum once at the end. The key -> k-slot assignment of the second product follows the score layout
-// (lane half hh holds keys 8j + 4hh .. +3), so P^T needs no data movement.
+// exchange the row max only when a tile moves the running reference max, and the row sum once at the end.
+// The key -> k-slot assignment of the second product follows the score layout (lane half hh holds keys
+// 8j + 4hh .. +3), so P^T needs no data movement.
 #pragma once
 
 #include "pa_launch.h"
