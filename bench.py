@@ -71,7 +71,7 @@ def algorithmic_work(wl, step, out_bytes: int):
 # Sources of the attention kernels each workload kind runs, and the kernels of one attention call: a traffic
 # summary taken on other sources is stale and not reported.
 ATTN_SOURCES = {"decode": ("pa_decode_stream.hip", "pa_decode_tile.h", "pa_common.h", "pa_api.hip"),
-                "prefill": ("pa_prefill.hip", "pa_common.h")}
+                "prefill": ("pa_prefill.hip", "pa_prefill_tile.h", "pa_common.h", "pa_api.hip")}
 ATTN_KERNELS = {"decode": ("decode_stream_kernel", "decode_stream_merge_kernel"), "prefill": ("prefill_mfma_kernel",)}
 
 
