@@ -1,0 +1,83 @@
+"""Store + decode captured once in a HIP graph and replayed with new inputs.
+
+Every call of the library only enqueues work on the caller's stream, with grids computed from host scalars
+(batch, table width, block size), no allocation, no memset and no host read of device data, so one capture
+serves later decode steps of the same batch size whose lengths, slots, queries and new K/V change in device
+memory (the engine captures only its decode step and replays it with new data copied into fixed tensors,
+"一个 prompt 的一生：nano-vllm 从起服务到吐出 token" §2.2.4).
+Each replay is checked bit for bit against the same calls run eagerly on a second copy of the cache pool, with
+eager work and synchronisations between replays.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import paged_kv_cache_111_amd as pa
+from harness import DEV
+
+HQ, HKV, D, BS = 16, 8, 128, 256
+
+
+def _bf16(rng, shape):
+    x = torch.from_numpy(rng.standard_normal(shape, dtype=np.float32))
+    return x.to(torch.bfloat16)
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("batch,split", [(1, 0), (4, 0), (16, 0), (8, 256)])
+def test_graph_store_decode_replays(batch, split):
+    rng = np.random.default_rng(900 + batch + split)
+    mbps = 8                                   # up to 2048 keys per sequence
+    nb = batch * mbps + 4
+    perm = rng.permutation(nb).astype(np.int32)
+    table = perm[: batch * mbps].reshape(batch, mbps)
+    pool_k = _bf16(rng, (nb, BS, HKV, D))
+    pool_v = _bf16(rng, (nb, BS, HKV, D))
+    kc_g, vc_g = pool_k.to(DEV), pool_v.to(DEV)
+    kc_e, vc_e = kc_g.clone(), vc_g.clone()
+
+    # static device buffers the graph reads
+    q = torch.empty((batch, HQ, D), dtype=torch.bfloat16, device=DEV)
+    k_new = torch.empty((batch, HKV, D), dtype=torch.bfloat16, device=DEV)
+    v_new = torch.empty_like(k_new)
+    slots = torch.empty(batch, dtype=torch.int32, device=DEV)
+    ctx = torch.empty(batch, dtype=torch.int32, device=DEV)
+    bt = torch.from_numpy(table).to(DEV)
+    out_g = torch.empty((batch, HQ, D), dtype=torch.float32, device=DEV)
+    out_e = torch.empty_like(out_g)
+    need = pa.decode_workspace_bytes(batch, HQ, HKV, D, mbps, BS, split)
+    ws_g = torch.empty(max(need, 16), dtype=torch.uint8, device=DEV)
+    ws_e = torch.empty_like(ws_g)
+    scale = 1.0 / np.sqrt(D)
+
+    def draw():
+        lens = rng.integers(1, mbps * BS + 1, size=batch).astype(np.int32)
+        pos = lens - 1
+        sl = (table[np.arange(batch), pos // BS].astype(np.int64) * BS + pos % BS).astype(np.int32)
+        q.copy_(_bf16(rng, (batch, HQ, D)).to(DEV))
+        k_new.copy_(_bf16(rng, (batch, HKV, D)).to(DEV))
+        v_new.copy_(_bf16(rng, (batch, HKV, D)).to(DEV))
+        slots.copy_(torch.from_numpy(sl).to(DEV))
+        ctx.copy_(torch.from_numpy(lens).to(DEV))
+        torch.cuda.synchronize()
+
+    def step(kc, vc, out, ws):
+        pa.store_kvcache(k_new, v_new, kc, vc, slots)
+        pa.decode(q, kc, vc, ctx, bt, scale, out=out, split_tokens=split, workspace=ws)
+
+    draw()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step(kc_g, vc_g, out_g, ws_g)
+    torch.cuda.synchronize()
+    for r in range(4):
+        if r > 0:
+            draw()
+        g.replay()
+        torch.cuda.synchronize()
+        step(kc_e, vc_e, out_e, ws_e)
+        torch.cuda.synchronize()
+        assert torch.isfinite(out_e).all(), f"replay {r}: eager output not finite"
+        assert torch.equal(out_g, out_e), f"replay {r}: graph output differs from the eager calls"
+        assert torch.equal(kc_g, kc_e) and torch.equal(vc_g, vc_e), f"replay {r}: caches differ"
