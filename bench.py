@@ -245,6 +245,72 @@ def time_workload(g: GpuWorkload, steps: int, warmup: int, n_layers: int):
             "attn_ms_min": float(np.min(attn_ms))}
 
 
+def graph_ladder(batches, iters: int = 200):
+    """Host launch overhead of a decode step (store_kvcache + decode) at the Qwen3-0.6B attention shape: wall
+    time per step of eager calls through the binding against one replay of the same calls captured in a HIP
+    graph, for a ladder of batch sizes (contexts U{128..4096}, block size 256, one pool, synthetic data). The
+    engine captures its decode step per batch size for exactly this overhead ("一个 prompt 的一生：nano-vllm 从起服务到吐出
+    token" §2.2.4)."""
+    import torch
+
+    import paged_kv_cache_111_amd as pa
+
+    dev = "cuda:0"
+    Hq, Hkv, D, bs, mbps = 16, 8, 128, 256, 16
+    rows = []
+    for B in batches:
+        rng = np.random.default_rng(7000 + B)
+        nb = B * mbps
+        table = rng.permutation(nb).astype(np.int32).reshape(B, mbps)
+        lens = rng.integers(128, mbps * bs + 1, size=B)
+        pos = lens - 1
+        slots = (table[np.arange(B), pos // bs].astype(np.int64) * bs + pos % bs).astype(np.int32)
+        gen = torch.Generator(device=dev).manual_seed(B)
+        kc = torch.randn((nb, bs, Hkv, D), device=dev, generator=gen).to(torch.bfloat16)
+        vc = torch.randn((nb, bs, Hkv, D), device=dev, generator=gen).to(torch.bfloat16)
+        q = torch.randn((B, Hq, D), device=dev, generator=gen).to(torch.bfloat16)
+        k_new = torch.randn((B, Hkv, D), device=dev, generator=gen).to(torch.bfloat16)
+        v_new = torch.randn((B, Hkv, D), device=dev, generator=gen).to(torch.bfloat16)
+        ctx = torch.from_numpy(lens.astype(np.int32)).to(dev)
+        sl = torch.from_numpy(slots).to(dev)
+        bt = torch.from_numpy(table).to(dev)
+        out = torch.empty((B, Hq, D), dtype=torch.bfloat16, device=dev)
+        ws = torch.empty(max(16, pa.decode_workspace_bytes(B, Hq, Hkv, D, mbps, bs, 0)), dtype=torch.uint8,
+                         device=dev)
+        scale = 1.0 / np.sqrt(D)
+
+        def step():
+            pa.store_kvcache(k_new, v_new, kc, vc, sl)
+            pa.decode(q, kc, vc, ctx, bt, scale, out=out, workspace=ws)
+
+        for _ in range(10):
+            step()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(iters):
+            step()
+        torch.cuda.synchronize()
+        eager = (time.perf_counter() - t0) / iters
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step()
+        for _ in range(10):
+            g.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(iters):
+            g.replay()
+        torch.cuda.synchronize()
+        graph = (time.perf_counter() - t0) / iters
+        kv = float(lens.sum()) * 2 * Hkv * D * 2
+        rows.append({"batch": B, "eager_us": round(eager * 1e6, 2), "graph_us": round(graph * 1e6, 2),
+                     "kv_GBps_eager": round(kv / eager / 1e9, 1), "kv_GBps_graph": round(kv / graph / 1e9, 1)})
+        print(f"[bench] graph ladder {rows[-1]}", file=sys.stderr, flush=True)
+        del g, kc, vc
+        torch.cuda.empty_cache()
+    return rows
+
+
 # ---------------------------------------------------------------------------------------------- CPU baseline
 
 
@@ -340,6 +406,8 @@ def main() -> int:
     ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"), default=None,
                     help="write the HBM traffic summary of --only's workload from two rocprofv3 counter files "
                          "(no GPU needed) and exit")
+    ap.add_argument("--graph-ladder", action="store_true",
+                    help="only time a decode step eager vs captured in a HIP graph over batch sizes 1..256")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 1 GiB copy kernel (reference for the HBM byte counters)")
     args = ap.parse_args()
@@ -355,6 +423,9 @@ def main() -> int:
     import torch
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.graph_ladder:
+        print(json.dumps({"graph_ladder": graph_ladder([1, 2, 4, 8, 16, 32, 64, 128, 256])}))
+        return 0
     main_name = args.only or "decode_qwen3_0p6b"
     wl, main = bench_one(main_name, args.steps, args.warmup, args.layers, args.out_dtype)
     print(f"[bench] {main_name}: {json.dumps(main['timing'])}", file=sys.stderr, flush=True)

@@ -19,6 +19,17 @@ namespace pa {
 
 constexpr int kStreamWaves = 4;                       // workers per workgroup (they share the prefix sums)
 constexpr int kSlotFloats = 16 + 16 + 16 * 128;       // one partial: m[16], l[16], O[16][128] (G <= 16)
+#ifndef PA_STREAM_MIN_CHUNK
+#define PA_STREAM_MIN_CHUNK 128
+#endif
+constexpr int64_t kMinChunk = PA_STREAM_MIN_CHUNK;    // keys per slice at least (a multiple of 32): on small calls
+                                                      // fewer workers, and fewer partials per cut pair
+
+// Keys per worker slice: an equal share of the padded total, rounded up to 32, at least kMinChunk. The decode
+// pass and the merge compute it the same way.
+__device__ __forceinline__ int64_t stream_chunk(int64_t total, int32_t n_workers) {
+  return max(((total + n_workers - 1) / n_workers + 31) & ~int64_t(31), kMinChunk);
+}
 
 #ifndef PA_STREAM_NBUF
 #define PA_STREAM_NBUF 2
@@ -117,7 +128,7 @@ __global__ __launch_bounds__(64 * kStreamWaves) __attribute__((amdgpu_waves_per_
 
   const int64_t Tp = __builtin_amdgcn_readfirstlane(cum[batch]);
   const int64_t total = Tp * Hkv;
-  const int64_t chunk = ((total + n_workers - 1) / n_workers + 31) & ~int64_t(31);
+  const int64_t chunk = stream_chunk(total, n_workers);
   const int wave = __builtin_amdgcn_readfirstlane(int(threadIdx.x >> 6));
   const int wid = int(blockIdx.x) * kStreamWaves + wave;
   const int64_t u0 = int64_t(wid) * chunk;
@@ -245,7 +256,8 @@ __global__ __launch_bounds__(64 * kStreamWaves) __attribute__((amdgpu_waves_per_
 // left a partial (slot 0 if the pair is the first piece of the worker's slice, else slot 1). For each query
 // head: M = max m_i, L = sum l_i 2^(m_i - M), O = sum O_i 2^(m_i - M) / L. One wave per (sequence, query head);
 // pairs inside one slice return. The rows of the first eight partials are loaded together with every partial's
-// (m, l) (lane j holds partial j's, 64 at a time), so most pairs take one round of dependent loads.
+// (m, l) (lane j holds partial j's, 64 at a time), so most pairs take one round of dependent loads; further
+// rows are read eight at a time.
 constexpr int kMergeEager = 8;
 
 __global__ __launch_bounds__(64) void decode_stream_merge_kernel(const int32_t* __restrict__ ctx_lens, int32_t batch,
@@ -268,7 +280,7 @@ __global__ __launch_bounds__(64) void decode_stream_merge_kernel(const int32_t* 
     all += __shfl_xor(all, off, 64);
   }
   const int64_t total = all * Hkv;
-  const int64_t chunk = ((total + n_workers - 1) / n_workers + 31) & ~int64_t(31);
+  const int64_t chunk = stream_chunk(total, n_workers);
   const int64_t a = int64_t(h) * all + before;
   const int64_t b = a + ((ctx_lens[s] + 31) & ~31);
   if (b == a) return;  // no keys (lengths are documented >= 1)
@@ -307,12 +319,12 @@ __global__ __launch_bounds__(64) void decode_stream_merge_kernel(const int32_t* 
       Ls += wave_sum(wj * lj);
     }
     int k = jb == 0 ? kMergeEager : 0;
-    for (; k + 4 <= nb; k += 4) {
-      float2 r[4];
+    for (; k + 8 <= nb; k += 8) {
+      float2 r[8];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) r[e] = *reinterpret_cast<const float2*>(part_of(jb + k + e) + 32 + g * 128 + 2 * lane);
+      for (int e = 0; e < 8; ++e) r[e] = *reinterpret_cast<const float2*>(part_of(jb + k + e) + 32 + g * 128 + 2 * lane);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
+      for (int e = 0; e < 8; ++e) {
         const float w = __shfl(wj, k + e, 64);
         a0 += w * r[e].x;
         a1 += w * r[e].y;
