@@ -311,6 +311,45 @@ def graph_ladder(batches, iters: int = 200):
     return rows
 
 
+def store_sweep(tokens=(64, 2048, 16384, 131072), iters: int = 50):
+    """store_kvcache bandwidth at the Qwen3-0.6B cache shape (Hkv 8, D 128, bf16, block size 256) over token
+    counts: decode-size stores are launch-bound, large ones HBM-bound. Bytes = 2·T·Hkv·D·2 read + the same
+    written + 4T of slots; slots are a random permutation of a pool twice the size (no duplicates)."""
+    import torch
+
+    import paged_kv_cache_111_amd as pa
+
+    dev = "cuda:0"
+    Hkv, D, bs = 8, 128, 256
+    rows = []
+    for T in tokens:
+        nb = max(8, (2 * T + bs - 1) // bs)
+        rng = np.random.default_rng(5000 + T)
+        slots = torch.from_numpy(rng.permutation(nb * bs)[:T].astype(np.int32)).to(dev)
+        gen = torch.Generator(device=dev).manual_seed(T)
+        k = torch.randn((T, Hkv, D), device=dev, generator=gen).to(torch.bfloat16)
+        v = torch.randn((T, Hkv, D), device=dev, generator=gen).to(torch.bfloat16)
+        kc = torch.zeros((nb, bs, Hkv, D), dtype=torch.bfloat16, device=dev)
+        vc = torch.zeros_like(kc)
+        for _ in range(5):
+            pa.store_kvcache(k, v, kc, vc, slots)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(iters):
+            pa.store_kvcache(k, v, kc, vc, slots)
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / iters
+        nbytes = 2 * (2 * T * Hkv * D * 2) + 4 * T
+        rows.append({"tokens": T, "us": round(us, 2), "GBps": round(nbytes / us / 1e3, 1),
+                     "frac_hbm": round(nbytes / us / 1e3 / HBM_PEAK_GBS, 4)})
+        print(f"[bench] store sweep {rows[-1]}", file=sys.stderr, flush=True)
+        del kc, vc, k, v
+        torch.cuda.empty_cache()
+    return rows
+
+
 # ---------------------------------------------------------------------------------------------- CPU baseline
 
 
@@ -406,6 +445,8 @@ def main() -> int:
     ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"), default=None,
                     help="write the HBM traffic summary of --only's workload from two rocprofv3 counter files "
                          "(no GPU needed) and exit")
+    ap.add_argument("--store-sweep", action="store_true",
+                    help="only time store_kvcache at the 0.6B cache shape for 64 .. 131072 tokens")
     ap.add_argument("--graph-ladder", action="store_true",
                     help="only time a decode step eager vs captured in a HIP graph over batch sizes 1..256")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -423,6 +464,9 @@ def main() -> int:
     import torch
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.store_sweep:
+        print(json.dumps({"store_sweep": store_sweep()}))
+        return 0
     if args.graph_ladder:
         print(json.dumps({"graph_ladder": graph_ladder([1, 2, 4, 8, 16, 32, 64, 128, 256])}))
         return 0
