@@ -126,13 +126,16 @@ __global__ __launch_bounds__(kPreThreads) __attribute__((amdgpu_waves_per_eu(2, 
   const int va_off = (4 * (g4 >> 1) + (li >> 2)) * kVRow + 16 * (g4 & 1) + 4 * (li & 3);
 
   u32x4 kst[kPieces], vst[kPieces];
-  // prologue: K tiles 0 and 1, V tile 0 in LDS; scores of tile 0
-  pf_gload1<kAligned, kPow2>(kst, kbase, table, 0, k_len, bs, bs_shift, row_bytes, tid);
-  pf_gload1<kAligned, kPow2>(vst, vbase, table, 0, k_len, bs, bs_shift, row_bytes, tid);
-  pf_lstore_k(kst, kt[0], tid);
-  pf_lstore_v(vst, vt[0], tid);
-  pf_gload1<kAligned, kPow2>(kst, kbase, table, kPreKeys, k_len, bs, bs_shift, row_bytes, tid);
-  pf_lstore_k(kst, kt[1], tid);
+  // prologue: K tiles 0 and 1, V tile 0 in LDS (their loads issued together: one round trip); scores of tile 0
+  {
+    u32x4 k1st[kPieces];
+    pf_gload1<kAligned, kPow2>(kst, kbase, table, 0, k_len, bs, bs_shift, row_bytes, tid);
+    pf_gload1<kAligned, kPow2>(vst, vbase, table, 0, k_len, bs, bs_shift, row_bytes, tid);
+    pf_gload1<kAligned, kPow2>(k1st, kbase, table, kPreKeys, k_len, bs, bs_shift, row_bytes, tid);
+    pf_lstore_k(kst, kt[0], tid);
+    pf_lstore_v(vst, vt[0], tid);
+    pf_lstore_k(k1st, kt[1], tid);
+  }
   __syncthreads();
   f32x16 sa[kSub], sb[kSub];
   pf_scores(sa, kt[0], ka_off, qb);
