@@ -30,7 +30,8 @@ namespace pa {
 
 constexpr int kPreRows = 128;  // query rows per workgroup
 
-// Scheduling hints (instruction groups in issue order) for the two long blocks of a step.
+// Scheduling hints (instruction groups in issue order) for the two long blocks of a step; the ratios were
+// chosen by timing (three vector instructions per score MFMA measured best of 1-4).
 // Mask bits: 0x2 VALU, 0x8 MFMA, 0x20 VMEM read, 0x100 DS read, 0x200 DS write.
 __device__ __forceinline__ void pf_sched_scores() {
   __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
@@ -38,7 +39,7 @@ __device__ __forceinline__ void pf_sched_scores() {
   for (int i = 0; i < 16; ++i) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
     __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
   }
 }
 __device__ __forceinline__ void pf_sched_weights_pv() {
