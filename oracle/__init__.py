@@ -6,7 +6,9 @@ Only the tests, the smoke check and the benchmark's CPU-baseline leg may import 
 It is the plain definition of what the step computes, written out in NumPy float64:
   * the slot arithmetic and block-count rules printed on the pages (metadata.py);
   * store_kvcache as a scatter into the flat slot view of the pool, and the block-table gather (paged.py);
-  * naive softmax(Q K^T * scale + causal mask) V per query head (paged.py).
+  * naive softmax(Q K^T * scale + causal mask) V per query head (paged.py);
+  * the pre-attention step of the new tokens: q_norm/k_norm RMSNorm, rotary embedding by table lookup, and
+    the store of the rotated K and of V (rope.py).
 """
 
 from .metadata import (  # noqa: F401
@@ -25,4 +27,11 @@ from .paged import (  # noqa: F401
     prefill_varlen,
     decode,
     run_step,
+)
+from .rope import (  # noqa: F401
+    rms_norm,
+    rope_rotate_half,
+    norm_rope,
+    round_to,
+    norm_rope_store,
 )

@@ -3,7 +3,8 @@
 This package only draws random numbers and lays them out the way an inference engine's block manager and
 scheduler would hand them to the attention layer: sequence lengths, how many tokens of each sequence already
 have K/V in the cache, the physical block ids given to each sequence, and the Q/K/V values. It computes none of
-the method's arithmetic: no slot addresses, no prefix sums, no masks, no attention. The CPU oracle and the HIP
+the method's arithmetic: no slot addresses, no prefix sums, no masks, no attention, no normalisation or
+rotation (the rotary table itself is a model constant and is drawn here as an input). The CPU oracle and the HIP
 path each derive those themselves from what is drawn here. Both read these arrays; neither shares code through
 this package.
 
@@ -21,4 +22,5 @@ from .gen import (  # noqa: F401
     build_prefill,
     build_decode,
     encode_values,
+    build_rope_inputs,
 )

@@ -356,6 +356,32 @@ _BUILDERS = {
 }
 
 
+def build_rope_inputs(seed: int, num_tokens: int, num_heads: int, num_kv_heads: int, head_dim: int, dtype: str,
+                      max_position: int, base: float = 1.0e6, positions=None) -> dict:
+    """Inputs of the pre-attention step of num_tokens new tokens: q [T, Hq, D], k, v [T, Hkv, D] ~ N(0, 1), the
+    q_norm / k_norm weights [D] ~ N(1, 0.1), token positions (drawn below max_position unless given), and the
+    rotary table [max_position, D] float32 a model precomputes: cos of position * base^(-2i/D) for i < D/2 in the
+    first half of a row, the sin in the second half (base 1e6 as in Qwen3's published configuration; the pages
+    name the table lookup but not its constants)."""
+    rng = np.random.default_rng([seed, 7])
+    if positions is None:
+        positions = rng.integers(0, max_position, size=num_tokens)
+    positions = np.asarray(positions, dtype=np.int32)
+    inv_freq = base ** (-np.arange(0, head_dim, 2, dtype=np.float64) / head_dim)
+    ang = np.arange(max_position, dtype=np.float64)[:, None] * inv_freq[None, :]
+    cos_sin = np.concatenate([np.cos(ang), np.sin(ang)], axis=1).astype(np.float32)
+    return {
+        "q": encode_values(rng.standard_normal((num_tokens, num_heads, head_dim)), dtype),
+        "k": encode_values(rng.standard_normal((num_tokens, num_kv_heads, head_dim)), dtype),
+        "v": encode_values(rng.standard_normal((num_tokens, num_kv_heads, head_dim)), dtype),
+        "q_weight": encode_values(1.0 + 0.1 * rng.standard_normal(head_dim), dtype),
+        "k_weight": encode_values(1.0 + 0.1 * rng.standard_normal(head_dim), dtype),
+        "positions": positions,
+        "cos_sin": cos_sin,
+        "eps": 1e-6,
+    }
+
+
 _SEEDS = {"tiny": 101, "decode_qwen3_0p6b": 102, "prefill_qwen3_8b": 103, "decode_qwen3_32b": 104,
           "chunked_qwen3_8b": 105}
 
