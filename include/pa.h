@@ -103,6 +103,37 @@ pa_status pa_store_kvcache(const void* k, int64_t k_tok_stride, const void* v, i
                            pa_dtype dtype, void* stream);
 
 /*
+ * pa_norm_rope_store_kvcache -- the layer's pre-attention step for the new tokens in one pass: k_norm, rotary
+ * embedding and the store of K (and V) into the cache, plus q_norm and rotary embedding of Q when q is given.
+ *
+ * The layer runs q_norm -> k_norm -> rope -> store_kvcache before attention ("一个 prompt 的一生" §2.2.4, the
+ * operators of one decoder layer), the rotation by table lookup (same page §3.3.2). Per token i and head h
+ * (the pages name the steps; the formulas are the usual ones and are stated here):
+ *   y = x / sqrt(mean over d of x[d]^2 + rms_eps) * weight[d]                      (RMSNorm over head_dim)
+ *   out[d]       = y[d] * cos[d] - y[d + D/2] * sin[d]    for d < D/2               (rotate half)
+ *   out[d + D/2] = y[d + D/2] * cos[d] + y[d] * sin[d]
+ * with cos = cos_sin[pos][0 .. D/2), sin = cos_sin[pos][D/2 .. D) and pos = positions[i] (clamped to
+ * [0, max_position - 1]). For slot_mapping[i] >= 0 the rotated key goes to flat_k_cache[slot] and v[i] to
+ * flat_v_cache[slot] unchanged; negative slots store nothing. Arithmetic is fp32; bf16 results are rounded to
+ * nearest even.
+ *   k, v           (device) [num_tokens, num_kv_heads, head_dim], token stride *_tok_stride elements
+ *   k_norm_weight  (device) [head_dim], dtype
+ *   q              (device) [num_tokens, num_heads, head_dim] or NULL (then q_norm_weight, q_out and
+ *                  num_heads are ignored)
+ *   q_norm_weight  (device) [head_dim]; q_out (device) [num_tokens, num_heads, head_dim], contiguous, dtype
+ *   positions      (device) [num_tokens] int32; cos_sin (device) [max_position, head_dim] float32
+ *   k_cache, v_cache, slot_mapping as for pa_store_kvcache
+ * head_dim must be a power of two in 16 .. 512; rms_eps >= 0; every pointer and token stride 16-byte aligned.
+ */
+pa_status pa_norm_rope_store_kvcache(const void* k, int64_t k_tok_stride, const void* v, int64_t v_tok_stride,
+                                     const void* k_norm_weight, const void* q, int64_t q_tok_stride,
+                                     const void* q_norm_weight, void* q_out, int32_t num_heads, float rms_eps,
+                                     const int32_t* positions, const float* cos_sin, int32_t max_position,
+                                     void* k_cache, void* v_cache, const int32_t* slot_mapping, int32_t num_tokens,
+                                     int32_t num_kv_heads, int32_t head_dim, int32_t num_blocks,
+                                     int32_t block_size, pa_dtype dtype, void* stream);
+
+/*
  * pa_prefill_varlen -- causal attention of the new tokens of `batch` sequences over the paged cache.
  *
  * For sequence s, rows cu_seqlens_q[s] .. cu_seqlens_q[s+1]-1 of q attend to its

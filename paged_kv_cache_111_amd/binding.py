@@ -33,6 +33,10 @@ SIGNATURES = {
                                          _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr]),
     "pa_store_kvcache": (ctypes.c_int, [_c_ptr, _c_i64, _c_ptr, _c_i64, _c_ptr, _c_ptr, _c_ptr, _c_i32, _c_i32,
                                         _c_i32, _c_i32, _c_i32, ctypes.c_int, _c_ptr]),
+    "pa_norm_rope_store_kvcache": (ctypes.c_int, [_c_ptr, _c_i64, _c_ptr, _c_i64, _c_ptr, _c_ptr, _c_i64, _c_ptr,
+                                                  _c_ptr, _c_i32, _c_f32, _c_ptr, _c_ptr, _c_i32, _c_ptr, _c_ptr,
+                                                  _c_ptr, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, ctypes.c_int,
+                                                  _c_ptr]),
     "pa_prefill_varlen": (ctypes.c_int, [_c_ptr, _c_i64, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_i32, _c_i32,
                                          _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_f32,
                                          ctypes.c_int, _c_ptr, ctypes.c_int, _c_ptr, _c_size, _c_ptr]),
@@ -154,6 +158,41 @@ def store_kvcache(k, v, k_cache, v_cache, slot_mapping, stream=None) -> None:
     st = lib().pa_store_kvcache(_ptr(k), ks, _ptr(v), vs, _ptr(k_cache), _ptr(v_cache), _ptr(slot_mapping), T, hkv,
                                 d, nb, bs, _dtype_code(k_cache.dtype), _stream(stream))
     _check("pa_store_kvcache", st)
+
+
+def norm_rope_store_kvcache(k, v, k_cache, v_cache, slot_mapping, k_norm_weight, positions, cos_sin,
+                            rms_eps: float = 1e-6, q=None, q_norm_weight=None, q_out=None, stream=None):
+    """pa_norm_rope_store_kvcache: k_norm + rotary embedding of k stored at its slot, v stored as is; with q,
+    q_norm + rotary embedding into q_out ([T, Hq, D], allocated if None), which is returned."""
+    nb, bs, hkv, d = _cache_dims(k_cache, v_cache)
+    _require(k.dtype == k_cache.dtype and v.dtype == k_cache.dtype, "k/v must match the cache dtype")
+    _require(k_norm_weight.dtype == k_cache.dtype and tuple(k_norm_weight.shape) == (d,),
+             "k_norm_weight must be [head_dim] in the cache dtype")
+    ks = _token_rows(k, hkv, d, "k")
+    vs = _token_rows(v, hkv, d, "v")
+    _i32(slot_mapping, "slot_mapping")
+    _i32(positions, "positions")
+    _require(cos_sin.dtype == torch.float32 and cos_sin.is_contiguous() and cos_sin.dim() == 2 and
+             int(cos_sin.shape[1]) == d, "cos_sin must be contiguous float32 [max_position, head_dim]")
+    T = int(k.shape[0])
+    _require(v.shape[0] == T and slot_mapping.shape[0] == T and positions.shape[0] == T,
+             "k, v, slot_mapping and positions must have one row per token")
+    hq, qs = 0, 0
+    if q is not None:
+        _require(q.dtype == k_cache.dtype and q_norm_weight is not None and q_norm_weight.dtype == k_cache.dtype,
+                 "q and q_norm_weight must be in the cache dtype")
+        hq = int(q.shape[1])
+        qs = _token_rows(q, hq, d, "q")
+        if q_out is None:
+            q_out = torch.empty((T, hq, d), dtype=q.dtype, device=q.device)
+        _require(q_out.is_contiguous() and tuple(q_out.shape) == (T, hq, d), "q_out must be contiguous [T, Hq, D]")
+    st = lib().pa_norm_rope_store_kvcache(_ptr(k), ks, _ptr(v), vs, _ptr(k_norm_weight), _ptr(q), qs,
+                                          _ptr(q_norm_weight), _ptr(q_out), hq, float(rms_eps), _ptr(positions),
+                                          _ptr(cos_sin), int(cos_sin.shape[0]), _ptr(k_cache), _ptr(v_cache),
+                                          _ptr(slot_mapping), T, hkv, d, nb, bs, _dtype_code(k_cache.dtype),
+                                          _stream(stream))
+    _check("pa_norm_rope_store_kvcache", st)
+    return q_out
 
 
 def prefill_workspace_bytes(batch, num_heads, head_dim, max_seqlen_q, max_seqlen_k) -> int:

@@ -119,6 +119,39 @@ pa_status pa_store_kvcache(const void* k, int64_t k_tok_stride, const void* v, i
   return launched();
 }
 
+pa_status pa_norm_rope_store_kvcache(const void* k, int64_t k_tok_stride, const void* v, int64_t v_tok_stride,
+                                     const void* k_norm_weight, const void* q, int64_t q_tok_stride,
+                                     const void* q_norm_weight, void* q_out, int32_t num_heads, float rms_eps,
+                                     const int32_t* positions, const float* cos_sin, int32_t max_position,
+                                     void* k_cache, void* v_cache, const int32_t* slot_mapping, int32_t num_tokens,
+                                     int32_t num_kv_heads, int32_t head_dim, int32_t num_blocks,
+                                     int32_t block_size, pa_dtype dtype, void* stream) {
+  if (!valid_dtype(dtype)) return PA_ERR_UNSUPPORTED;
+  if (head_dim < 16 || head_dim > 512 || (head_dim & (head_dim - 1))) return PA_ERR_UNSUPPORTED;
+  if (num_tokens < 0 || num_kv_heads <= 0 || num_blocks <= 0 || block_size <= 0 || max_position <= 0)
+    return PA_ERR_SHAPE;
+  if (!(rms_eps >= 0.f) || rms_eps > 3.0e38f) return PA_ERR_SHAPE;
+  if (int64_t(num_blocks) * block_size > kInt32Max) return PA_ERR_SHAPE;
+  const int64_t row = int64_t(num_kv_heads) * head_dim;
+  if (k_tok_stride < row || v_tok_stride < row) return PA_ERR_SHAPE;
+  if (q && (num_heads <= 0 || q_tok_stride < int64_t(num_heads) * head_dim)) return PA_ERR_SHAPE;
+  if (num_tokens == 0) return PA_OK;
+  if (!k || !v || !k_norm_weight || !positions || !cos_sin || !k_cache || !v_cache || !slot_mapping)
+    return PA_ERR_NULL;
+  if (q && (!q_norm_weight || !q_out)) return PA_ERR_NULL;
+  const int eb = elem_bytes(dtype);
+  if ((k_tok_stride * eb) % 16 || (v_tok_stride * eb) % 16 || (q && (q_tok_stride * eb) % 16)) return PA_ERR_SHAPE;
+  if (!aligned(k, 16) || !aligned(v, 16) || !aligned(k_norm_weight, 16) || !aligned(cos_sin, 16) ||
+      !aligned(k_cache, 16) || !aligned(v_cache, 16))
+    return PA_ERR_SHAPE;
+  if (q && (!aligned(q, 16) || !aligned(q_norm_weight, 16) || !aligned(q_out, 16))) return PA_ERR_SHAPE;
+  pa::launch_norm_rope_store(k, k_tok_stride, v, v_tok_stride, k_norm_weight, q, q_tok_stride, q_norm_weight, q_out,
+                             num_heads, rms_eps, positions, cos_sin, max_position, k_cache, v_cache, slot_mapping,
+                             num_tokens, num_kv_heads, head_dim, dtype == PA_BF16,
+                             static_cast<hipStream_t>(stream));
+  return launched();
+}
+
 size_t pa_prefill_workspace_bytes(int32_t batch, int32_t num_heads, int32_t head_dim, int32_t max_seqlen_q,
                                   int32_t max_seqlen_k) {
   (void)batch; (void)num_heads; (void)head_dim; (void)max_seqlen_q; (void)max_seqlen_k;

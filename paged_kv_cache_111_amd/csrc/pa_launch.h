@@ -13,6 +13,12 @@ void launch_store_kvcache(const void* k, int64_t k_stride_bytes, const void* v, 
                           void* k_cache, void* v_cache, const int32_t* slot_mapping, int32_t num_tokens,
                           int64_t row_bytes, int vec_bytes, hipStream_t stream);
 
+void launch_norm_rope_store(const void* k, int64_t k_stride, const void* v, int64_t v_stride, const void* k_w,
+                            const void* q, int64_t q_stride, const void* q_w, void* q_out, int32_t Hq, float eps,
+                            const int32_t* positions, const float* cos_sin, int32_t max_position, void* k_cache,
+                            void* v_cache, const int32_t* slot_mapping, int32_t num_tokens, int32_t Hkv,
+                            int32_t D, bool bf16, hipStream_t stream);
+
 void launch_attn_generic(bool bf16, const void* q, int64_t q_stride, const void* k_cache, const void* v_cache,
                          const int32_t* cu_q, const int32_t* cu_k, const int32_t* ctx_lens,
                          const int32_t* block_table, int32_t mbps, int32_t batch, int32_t rows, int32_t Hq,

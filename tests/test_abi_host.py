@@ -146,3 +146,24 @@ def test_nonpositive_scale_is_rejected():
     assert _prefill(scale=float("nan")) == b.PA_ERR_SHAPE
     assert _decode(scale=0.0) == b.PA_ERR_SHAPE
     assert _decode(scale=float("inf")) == b.PA_ERR_SHAPE
+
+
+def _rope(**kw):
+    args = dict(k=NULL, ks=1024, v=NULL, vs=1024, kw=NULL, q=NULL, qs=2048, qw=NULL, qo=NULL, hq=16, eps=1e-6,
+                pos=NULL, cs=NULL, maxp=4096, kc=NULL, vc=NULL, sl=NULL, T=4, hkv=8, d=128, nb=16, bs=256,
+                dtype=1, st=NULL)
+    args.update(kw)
+    return pa.lib().pa_norm_rope_store_kvcache(*args.values())
+
+
+def test_norm_rope_store_rejects_bad_arguments():
+    assert _rope() == b.PA_ERR_NULL
+    assert _rope(T=0) == b.PA_OK
+    assert _rope(d=96) == b.PA_ERR_UNSUPPORTED       # not a power of two
+    assert _rope(d=8) == b.PA_ERR_UNSUPPORTED
+    assert _rope(dtype=4) == b.PA_ERR_UNSUPPORTED
+    assert _rope(eps=-1.0) == b.PA_ERR_SHAPE
+    assert _rope(eps=float("nan")) == b.PA_ERR_SHAPE
+    assert _rope(maxp=0) == b.PA_ERR_SHAPE
+    assert _rope(ks=100) == b.PA_ERR_SHAPE            # token stride shorter than a row
+    assert _rope(nb=2 ** 24, bs=256) == b.PA_ERR_SHAPE  # slot space beyond int32
