@@ -314,7 +314,8 @@ def graph_ladder(batches, iters: int = 200):
 def store_sweep(tokens=(64, 2048, 16384, 131072), iters: int = 50):
     """store_kvcache bandwidth at the Qwen3-0.6B cache shape (Hkv 8, D 128, bf16, block size 256) over token
     counts: decode-size stores are launch-bound, large ones HBM-bound. Bytes = 2·T·Hkv·D·2 read + the same
-    written + 4T of slots; slots are a random permutation of a pool twice the size (no duplicates)."""
+    written + 4T of slots; slots are a random permutation of a pool twice the size (no duplicates). Beside it,
+    the fused q/k norm + rotary embedding + store step with 16 query heads."""
     import torch
 
     import paged_kv_cache_111_amd as pa
@@ -342,10 +343,35 @@ def store_sweep(tokens=(64, 2048, 16384, 131072), iters: int = 50):
         torch.cuda.synchronize()
         us = e0.elapsed_time(e1) * 1e3 / iters
         nbytes = 2 * (2 * T * Hkv * D * 2) + 4 * T
+        # the fused pre-attention step at the same shape with Q (16 query heads): reads q, k, v, a table row and
+        # the position of each token, writes the rotated q, K and V
+        Hq = 16
+        q = torch.randn((T, Hq, D), device=dev, generator=gen).to(torch.bfloat16)
+        q_out = torch.empty_like(q)
+        kw = torch.ones(D, dtype=torch.bfloat16, device=dev)
+        pos = torch.from_numpy(rng.integers(0, 4096, size=T).astype(np.int32)).to(dev)
+        ang = torch.arange(4096, device=dev, dtype=torch.float64)[:, None] * \
+            (1e6 ** (-torch.arange(0, D, 2, device=dev, dtype=torch.float64) / D))[None, :]
+        cs = torch.cat([torch.cos(ang), torch.sin(ang)], dim=1).float().contiguous()
+
+        def fused():
+            pa.norm_rope_store_kvcache(k, v, kc, vc, slots, kw, pos, cs, 1e-6, q=q, q_norm_weight=kw, q_out=q_out)
+
+        for _ in range(5):
+            fused()
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(iters):
+            fused()
+        e1.record()
+        torch.cuda.synchronize()
+        us_f = e0.elapsed_time(e1) * 1e3 / iters
+        fbytes = 2 * T * (2 * Hkv + Hq) * D * 2 + T * D * 4 + 8 * T
         rows.append({"tokens": T, "us": round(us, 2), "GBps": round(nbytes / us / 1e3, 1),
-                     "frac_hbm": round(nbytes / us / 1e3 / HBM_PEAK_GBS, 4)})
+                     "frac_hbm": round(nbytes / us / 1e3 / HBM_PEAK_GBS, 4),
+                     "norm_rope_store_us": round(us_f, 2), "norm_rope_store_GBps": round(fbytes / us_f / 1e3, 1)})
         print(f"[bench] store sweep {rows[-1]}", file=sys.stderr, flush=True)
-        del kc, vc, k, v
+        del kc, vc, k, v, q, q_out
         torch.cuda.empty_cache()
     return rows
 
