@@ -8,7 +8,9 @@ It is the plain definition of what the step computes, written out in NumPy float
   * store_kvcache as a scatter into the flat slot view of the pool, and the block-table gather (paged.py);
   * naive softmax(Q K^T * scale + causal mask) V per query head (paged.py);
   * the pre-attention step of the new tokens: q_norm/k_norm RMSNorm, rotary embedding by table lookup, and
-    the store of the rotated K and of V (rope.py).
+    the store of the rotated K and of V (rope.py);
+  * next-token sampling with temperature, softmax and Gumbel-max, with its Philox counter-based generator
+    (sampler.py).
 """
 
 from .metadata import (  # noqa: F401
@@ -34,4 +36,10 @@ from .rope import (  # noqa: F401
     norm_rope,
     round_to,
     norm_rope_store,
+)
+from .sampler import (  # noqa: F401
+    philox4x32_10,
+    uniforms,
+    gumbel_scores,
+    sample,
 )
