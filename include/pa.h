@@ -192,6 +192,29 @@ int32_t pa_decode_split_tokens(int32_t batch, int32_t num_heads, int32_t num_kv_
 size_t pa_decode_workspace_bytes(int32_t batch, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
                                  int32_t max_blocks_per_seq, int32_t block_size, int32_t split_tokens);
 
+/*
+ * pa_sample -- the next token of each sequence from its logits: temperature, softmax and Gumbel-max.
+ *
+ * The sampler divides the logits by the temperature, takes the softmax and draws with Gumbel-max ("Nano-vLLM
+ * 架构详解" §2.4, sampling stage; "一个 prompt 的一生" §4). Since argmax_i (log softmax(l/T)_i + g_i) does not depend
+ * on the softmax's normaliser, tokens[b] = argmax_i (logits[b][i] * (1 / T_b) + g_i) with g_i = -ln(-ln u_i);
+ * T_b <= 0 is greedy (argmax_i logits[b][i]); ties go to the lower index. The uniforms come from Philox4x32-10
+ * (Salmon et al., SC 2011) with counter (i / 4, b, offset mod 2^32, offset div 2^32) and key (seed mod 2^32,
+ * seed div 2^32), word i % 4, u = ((x >> 9) + 1/2) * 2^-23: the same (seed, offset) gives the same tokens, and a
+ * new offset per step gives fresh draws.
+ *   logits       (device) [batch, vocab] float32, row b at element b * row_stride
+ *   temperatures (device) [batch] float32
+ *   tokens       (device) [batch] int32, written
+ *   workspace    (device) at least pa_sample_workspace_bytes(batch, vocab) bytes
+ * batch <= 65535. A row whose logits are all NaN gets token 0.
+ */
+pa_status pa_sample(const float* logits, int64_t row_stride, const float* temperatures, int32_t batch,
+                    int32_t vocab, uint64_t seed, uint64_t offset, int32_t* tokens, void* workspace,
+                    size_t workspace_bytes, void* stream);
+
+/* Workspace bytes pa_sample needs for these sizes. */
+size_t pa_sample_workspace_bytes(int32_t batch, int32_t vocab);
+
 #ifdef __cplusplus
 }
 #endif

@@ -7,8 +7,8 @@ The sampler divides the logits by the sequence's temperature, takes the softmax 
 trick ("Nano-vLLM 架构详解" §2.4, the sampling stage: temperature, softmax and Gumbel max; "一个 prompt 的一生"
 §4: lm_head -> logits -> Sampler (Gumbel-max) -> token ids). Gumbel-max: with g_i = -log(-log u_i) for
 independent uniforms u_i, argmax_i (log p_i + g_i) is distributed as p; since log p_i = l_i / T - logsumexp(l / T)
-and the second term is the same for every i, the token is argmax_i (l_i / T + g_i). Temperature 0 is read as
-greedy decoding (argmax_i l_i). Ties go to the lower index.
+and the second term is the same for every i, the token is argmax_i (l_i / T + g_i). A temperature of 0 (or
+below) is read as greedy decoding (argmax_i l_i). Ties go to the lower index.
 
 Random numbers: each side implements the same counter-based generator from its published definition, Philox4x32
 with 10 rounds (J. K. Salmon, M. A. Moraes, R. O. Dror, D. E. Shaw, "Parallel random numbers: as easy as 1, 2,
@@ -59,14 +59,14 @@ def uniforms(rows, vocab: int, seed: int, offset: int) -> np.ndarray:
 
 def gumbel_scores(logits: np.ndarray, temperatures, u: np.ndarray, dtype=np.float32) -> np.ndarray:
     """l_i / T + g_i with g_i = -log(-log u_i) per row ([B, V]), in the given precision: float32 takes the decision
-    the way the kernel does, float64 gives the exact values. Rows with T = 0 score the logits alone (greedy)."""
+    the way the kernel does, float64 gives the exact values. Rows with T <= 0 score the logits alone (greedy)."""
     l = np.asarray(logits, dtype=dtype)
     t = np.asarray(temperatures, dtype=np.float64).reshape(-1, 1)
     g = -np.log(-np.log(np.asarray(u, dtype=dtype)))
     with np.errstate(divide="ignore", invalid="ignore"):
         inv_t = (dtype(1.0) / t.astype(dtype)).astype(dtype)
         scores = l * inv_t + g
-    return np.where(t == 0.0, l, scores).astype(dtype)
+    return np.where(t <= 0.0, l, scores).astype(dtype)
 
 
 def sample(logits: np.ndarray, temperatures, seed: int, offset: int, dtype=np.float32, rows=None):

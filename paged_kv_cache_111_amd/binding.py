@@ -37,6 +37,9 @@ SIGNATURES = {
                                                   _c_ptr, _c_i32, _c_f32, _c_ptr, _c_ptr, _c_i32, _c_ptr, _c_ptr,
                                                   _c_ptr, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, ctypes.c_int,
                                                   _c_ptr]),
+    "pa_sample": (ctypes.c_int, [_c_ptr, _c_i64, _c_ptr, _c_i32, _c_i32, ctypes.c_uint64, ctypes.c_uint64, _c_ptr,
+                                 _c_ptr, _c_size, _c_ptr]),
+    "pa_sample_workspace_bytes": (_c_size, [_c_i32, _c_i32]),
     "pa_prefill_varlen": (ctypes.c_int, [_c_ptr, _c_i64, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_i32, _c_i32,
                                          _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_f32,
                                          ctypes.c_int, _c_ptr, ctypes.c_int, _c_ptr, _c_size, _c_ptr]),
@@ -193,6 +196,30 @@ def norm_rope_store_kvcache(k, v, k_cache, v_cache, slot_mapping, k_norm_weight,
                                           _stream(stream))
     _check("pa_norm_rope_store_kvcache", st)
     return q_out
+
+
+def sample_workspace_bytes(batch: int, vocab: int) -> int:
+    return int(lib().pa_sample_workspace_bytes(batch, vocab))
+
+
+def sample(logits, temperatures, seed: int, offset: int, tokens=None, workspace=None, stream=None):
+    """pa_sample: logits [B, V] float32 (row stride free), temperatures [B] float32 -> tokens [B] int32."""
+    _require(logits.dtype == torch.float32 and logits.dim() == 2 and logits.stride(1) == 1,
+             "logits must be float32 [B, V] with contiguous rows")
+    _require(temperatures.dtype == torch.float32 and temperatures.is_contiguous(), "temperatures must be float32")
+    B, V = int(logits.shape[0]), int(logits.shape[1])
+    _require(temperatures.numel() == B, "one temperature per row")
+    if tokens is None:
+        tokens = torch.empty(B, dtype=torch.int32, device=logits.device)
+    _i32(tokens, "tokens")
+    need = sample_workspace_bytes(B, V)
+    if workspace is None:
+        workspace = torch.empty(max(need, 8), dtype=torch.uint8, device=logits.device)
+    wbytes = workspace.numel() * workspace.element_size()
+    st = lib().pa_sample(_ptr(logits), int(logits.stride(0)), _ptr(temperatures), B, V, int(seed) & (2 ** 64 - 1),
+                         int(offset) & (2 ** 64 - 1), _ptr(tokens), _ptr(workspace), wbytes, _stream(stream))
+    _check("pa_sample", st)
+    return tokens
 
 
 def prefill_workspace_bytes(batch, num_heads, head_dim, max_seqlen_q, max_seqlen_k) -> int:

@@ -152,6 +152,24 @@ pa_status pa_norm_rope_store_kvcache(const void* k, int64_t k_tok_stride, const 
   return launched();
 }
 
+size_t pa_sample_workspace_bytes(int32_t batch, int32_t vocab) {
+  if (batch <= 0 || vocab <= 0) return 0;
+  return size_t(batch) * pa::sample_chunks(batch, vocab) * 2 * sizeof(float);
+}
+
+pa_status pa_sample(const float* logits, int64_t row_stride, const float* temperatures, int32_t batch,
+                    int32_t vocab, uint64_t seed, uint64_t offset, int32_t* tokens, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+  if (batch < 0 || batch > 65535 || vocab <= 0 || row_stride < vocab) return PA_ERR_SHAPE;
+  if (batch == 0) return PA_OK;
+  if (!logits || !temperatures || !tokens || !workspace) return PA_ERR_NULL;
+  if (workspace_bytes < pa_sample_workspace_bytes(batch, vocab)) return PA_ERR_WORKSPACE;
+  if (!aligned(workspace, 8)) return PA_ERR_SHAPE;
+  pa::launch_sample(logits, row_stride, temperatures, batch, vocab, seed, offset, tokens, workspace,
+                    static_cast<hipStream_t>(stream));
+  return launched();
+}
+
 size_t pa_prefill_workspace_bytes(int32_t batch, int32_t num_heads, int32_t head_dim, int32_t max_seqlen_q,
                                   int32_t max_seqlen_k) {
   (void)batch; (void)num_heads; (void)head_dim; (void)max_seqlen_q; (void)max_seqlen_k;

@@ -19,6 +19,11 @@ void launch_norm_rope_store(const void* k, int64_t k_stride, const void* v, int6
                             void* v_cache, const int32_t* slot_mapping, int32_t num_tokens, int32_t Hkv,
                             int32_t D, bool bf16, hipStream_t stream);
 
+int32_t sample_chunks(int32_t batch, int32_t vocab);
+void launch_sample(const float* logits, int64_t row_stride, const float* temperatures, int32_t batch,
+                   int32_t vocab, uint64_t seed, uint64_t offset, int32_t* tokens, void* workspace,
+                   hipStream_t stream);
+
 void launch_attn_generic(bool bf16, const void* q, int64_t q_stride, const void* k_cache, const void* v_cache,
                          const int32_t* cu_q, const int32_t* cu_k, const int32_t* ctx_lens,
                          const int32_t* block_table, int32_t mbps, int32_t batch, int32_t rows, int32_t Hq,

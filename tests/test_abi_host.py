@@ -167,3 +167,16 @@ def test_norm_rope_store_rejects_bad_arguments():
     assert _rope(maxp=0) == b.PA_ERR_SHAPE
     assert _rope(ks=100) == b.PA_ERR_SHAPE            # token stride shorter than a row
     assert _rope(nb=2 ** 24, bs=256) == b.PA_ERR_SHAPE  # slot space beyond int32
+
+
+def test_sample_rejects_bad_arguments():
+    lib = pa.lib()
+    assert lib.pa_sample(NULL, 100, NULL, 0, 100, 1, 0, NULL, NULL, 0, NULL) == b.PA_OK
+    assert lib.pa_sample(NULL, 100, NULL, 4, 100, 1, 0, NULL, NULL, 0, NULL) == b.PA_ERR_NULL
+    assert lib.pa_sample(NULL, 50, NULL, 4, 100, 1, 0, NULL, NULL, 0, NULL) == b.PA_ERR_SHAPE   # stride < vocab
+    assert lib.pa_sample(NULL, 100, NULL, 70000, 100, 1, 0, NULL, NULL, 0, NULL) == b.PA_ERR_SHAPE
+    assert lib.pa_sample(NULL, 100, NULL, 4, 0, 1, 0, NULL, NULL, 0, NULL) == b.PA_ERR_SHAPE
+    # the workspace holds one (score, index) pair per chunk of each row
+    ws = pa.sample_workspace_bytes(64, 151936)
+    assert ws > 0 and ws % (64 * 8) == 0
+    assert pa.sample_workspace_bytes(0, 10) == 0
