@@ -376,6 +376,38 @@ def store_sweep(tokens=(64, 2048, 16384, 131072), iters: int = 50):
     return rows
 
 
+def sample_sweep(batches=(1, 64, 256), vocab: int = 151936, iters: int = 50):
+    """pa_sample at the Qwen3 vocabulary: time per call (events over back-to-back calls) and the rate at which
+    it consumes logits (B·V·4 bytes; the uniforms are generated in the kernel, not read)."""
+    import torch
+
+    import paged_kv_cache_111_amd as pa
+
+    dev = "cuda:0"
+    rows = []
+    for B in batches:
+        gen = torch.Generator(device=dev).manual_seed(B)
+        logits = 3.0 * torch.randn((B, vocab), device=dev, generator=gen)
+        temps = torch.full((B,), 0.8, device=dev)
+        toks = torch.empty(B, dtype=torch.int32, device=dev)
+        ws = torch.empty(max(8, pa.sample_workspace_bytes(B, vocab)), dtype=torch.uint8, device=dev)
+        for i in range(5):
+            pa.sample(logits, temps, 1, i, tokens=toks, workspace=ws)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(iters):
+            pa.sample(logits, temps, 1, i, tokens=toks, workspace=ws)
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / iters
+        rows.append({"batch": B, "vocab": vocab, "us": round(us, 2),
+                     "logits_GBps": round(B * vocab * 4 / us / 1e3, 1),
+                     "Gsamples_per_s": round(B * vocab / us / 1e3, 1)})
+        print(f"[bench] sample sweep {rows[-1]}", file=sys.stderr, flush=True)
+    return rows
+
+
 # ---------------------------------------------------------------------------------------------- CPU baseline
 
 
@@ -473,6 +505,8 @@ def main() -> int:
                          "(no GPU needed) and exit")
     ap.add_argument("--store-sweep", action="store_true",
                     help="only time store_kvcache at the 0.6B cache shape for 64 .. 131072 tokens")
+    ap.add_argument("--sample-sweep", action="store_true",
+                    help="only time the sampler at the Qwen3 vocabulary for batch 1, 64, 256")
     ap.add_argument("--graph-ladder", action="store_true",
                     help="only time a decode step eager vs captured in a HIP graph over batch sizes 1..256")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -492,6 +526,9 @@ def main() -> int:
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     if args.store_sweep:
         print(json.dumps({"store_sweep": store_sweep()}))
+        return 0
+    if args.sample_sweep:
+        print(json.dumps({"sample_sweep": sample_sweep()}))
         return 0
     if args.graph_ladder:
         print(json.dumps({"graph_ladder": graph_ladder([1, 2, 4, 8, 16, 32, 64, 128, 256])}))
