@@ -125,6 +125,8 @@ PREFILL_CASES = [
     # 64-key blocks with one-key sequences and a chunk that starts inside a block
     (8, 4, 128, 24, "bf16", [100, 61, 130], [50, 0, 129]),
     (16, 8, 128, 64, "bf16", [500, 64, 65, 1], [436, 0, 1, 0]),
+    # block size 1 (every key its own block)
+    (8, 2, 128, 1, "bf16", [17, 5], [3, 0]),
 ]
 
 
@@ -151,6 +153,9 @@ DECODE_CASES = [
     (16, 1, 128, 32, "bf16", [1, 31, 32, 33, 5000], 0),
     (32, 8, 128, 64, "bf16", [int(x) for x in np.random.default_rng(7).integers(1, 600, 300)], 0),
     (8, 8, 128, 256, "bf16", [20000], 0),
+    # block size 1; 32 query heads per KV head (beyond the MFMA kernels' 16: the generic kernel)
+    (8, 2, 128, 1, "bf16", [17, 1, 40], 0),
+    (32, 1, 128, 16, "bf16", [50, 300], 0),
 ]
 
 
@@ -160,6 +165,22 @@ def test_decode_small(case):
     wl = build_decode(f"decode_small_{case}", 300 + case, Hq, Hkv, D, bs, dt, ctx,
                       num_blocks=sum(-(-n // bs) for n in ctx) + 2)
     _run_and_check(wl, split_tokens=split)
+
+
+@pytest.mark.parametrize("bs", [16, 256])
+def test_prefill_with_sequences_without_new_tokens(bs):
+    """Sequences with no new token in a prefill batch compute nothing and leave the others unchanged."""
+    kl, cached = ([40, 33, 70, 16], [40, 5, 70, 0]) if bs == 16 else ([300, 257, 512], [300, 0, 512])
+    wl = build_prefill(f"prefill_empty_{bs}", 610 + bs, 8, 2, 128, bs, "bf16", kl, cached,
+                       num_blocks=sum(-(-n // bs) for n in kl) + 2, allow_empty=True)
+    _run_and_check(wl)
+
+
+def test_decode_largest_batch():
+    """4096 sequences (the largest batch of the balanced decode's prefix sums) of 1..64 keys."""
+    ctx = [int(x) for x in np.random.default_rng(11).integers(1, 65, 4096)]
+    wl = build_decode("decode_4096", 620, 8, 2, 128, 32, "bf16", ctx, num_blocks=sum(-(-n // 32) for n in ctx) + 2)
+    _run_and_check(wl)
 
 
 def test_bf16_output():

@@ -147,16 +147,19 @@ def _pad_tables(tables, width: int | None = None) -> np.ndarray:
 
 
 def build_prefill(name, seed, num_heads, num_kv_heads, head_dim, block_size, dtype, k_lens, cached,
-                  num_blocks=None, outlier_p=0.0, scale=None, table_width=None, fill=True) -> Workload:
+                  num_blocks=None, outlier_p=0.0, scale=None, table_width=None, fill=True,
+                  allow_empty=False) -> Workload:
     """One varlen prefill step: sequence s has k_lens[s] tokens, of which cached[s] are already in the cache.
 
-    Physical ids are consecutive slices of a seeded permutation of the pool (random, distinct).
+    Physical ids are consecutive slices of a seeded permutation of the pool (random, distinct). With
+    allow_empty, a sequence may have no new token (cached[s] == k_lens[s]): it is in the batch but computes
+    nothing.
     """
     rng = np.random.default_rng(seed)
     k_lens = np.asarray(k_lens, dtype=np.int64)
     cached = np.asarray(cached, dtype=np.int64)
-    if np.any(cached < 0) or np.any(cached >= k_lens):
-        raise ValueError("need 0 <= cached < k_len for every sequence")
+    if np.any(cached < 0) or np.any(cached > k_lens) or (not allow_empty and np.any(cached == k_lens)):
+        raise ValueError("need 0 <= cached < k_len for every sequence (<= with allow_empty)")
     need = [_blocks_for(n, block_size) for n in k_lens]
     if num_blocks is None:
         num_blocks = max(1, sum(need))
