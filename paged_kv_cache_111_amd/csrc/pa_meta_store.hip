@@ -10,9 +10,10 @@ namespace pa {
 
 // ------------------------------------------------------------------------------------------------- metadata
 //
-// Every workgroup rebuilds the two prefix sums over the batch in LDS (batch <= 8192, a few hundred adds per
-// thread at most), then handles 256 tokens: a binary search for the token's sequence, its absolute position
-// and its slot. Workgroup 0 also writes cu_seqlens_q/k and context_lens.
+// Every workgroup rebuilds the two prefix sums over the batch in LDS (each thread sums a run of sequences, the
+// runs are scanned with wave shuffles and across the four waves), then handles 256 tokens: a binary search for
+// the token's sequence, its absolute position and its slot. Workgroup 0 also writes cu_seqlens_q/k and
+// context_lens.
 constexpr int kMetaThreads = 256;
 
 __global__ __launch_bounds__(kMetaThreads) void build_metadata_kernel(
@@ -23,9 +24,11 @@ __global__ __launch_bounds__(kMetaThreads) void build_metadata_kernel(
   extern __shared__ int32_t smem[];
   int32_t* cu_q = smem;                  // [batch + 1]
   int32_t* cu_k = smem + (batch + 1);    // [batch + 1]
-  __shared__ int32_t part_q[kMetaThreads], part_k[kMetaThreads];
+  __shared__ int32_t wave_q[kMetaThreads / 64], wave_k[kMetaThreads / 64];
 
   const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
   const int chunk = (batch + kMetaThreads - 1) / kMetaThreads;
   const int lo = min(batch, tid * chunk), hi = min(batch, lo + chunk);
   int32_t sq = 0, sk = 0;
@@ -34,24 +37,32 @@ __global__ __launch_bounds__(kMetaThreads) void build_metadata_kernel(
     sq += n;
     sk += num_cached[s] + n;
   }
-  part_q[tid] = sq;
-  part_k[tid] = sk;
-  __syncthreads();
-  if (tid == 0) {  // exclusive scan of the 256 per-thread sums
-    int32_t aq = 0, ak = 0;
-    for (int t = 0; t < kMetaThreads; ++t) {
-      const int32_t q = part_q[t], k = part_k[t];
-      part_q[t] = aq;
-      part_k[t] = ak;
-      aq += q;
-      ak += k;
+  // exclusive prefix of the per-thread sums: inclusive scan within each wave by shuffles, then across the waves
+  int32_t iq = sq, ik = sk;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int32_t vq = __shfl_up(iq, off, 64);
+    const int32_t vk = __shfl_up(ik, off, 64);
+    if (lane >= off) {
+      iq += vq;
+      ik += vk;
     }
+  }
+  if (lane == 63) {
+    wave_q[wave] = iq;
+    wave_k[wave] = ik;
+  }
+  if (tid == 0) {
     cu_q[0] = 0;
     cu_k[0] = 0;
   }
   __syncthreads();
-  sq = part_q[tid];
-  sk = part_k[tid];
+  sq = iq - sq;
+  sk = ik - sk;
+  for (int w = 0; w < wave; ++w) {
+    sq += wave_q[w];
+    sk += wave_k[w];
+  }
   for (int s = lo; s < hi; ++s) {
     const int32_t n = num_new[s];
     const int32_t kl = num_cached[s] + n;
