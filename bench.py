@@ -1,8 +1,8 @@
 """Benchmark of the paged-KV attention step on one MI355X.
 
-One step = one pass of the whole path over one batch: device-side metadata (slots, prefix sums), store_kvcache
-of the new tokens, then attention over the paged cache (decode: balanced pass + merge of cut sequences;
-prefill: one pass).
+One step = one pass of the whole path over one batch: device-side metadata (slots, prefix sums) and store_kvcache
+of the new tokens in one launch (two with --separate-store), then attention over the paged cache (decode:
+balanced pass + merge of cut sequences; prefill: one pass).
 
 Main line: the decode workload with Qwen3-0.6B attention shape (64 sequences, 16 query / 8 KV heads, head_dim
 128, bf16, block_size 256, contexts U[128, 4096]). Consecutive steps use different per-layer cache pools (the
@@ -163,12 +163,13 @@ def write_traffic_summary(workload: str, fetch_csv: str, write_csv: str) -> dict
 class GpuWorkload:
     """A workload's inputs on the device, with n_layers independent cache pools holding the same contents."""
 
-    def __init__(self, wl, n_layers: int, out_dtype):
+    def __init__(self, wl, n_layers: int, out_dtype, fused_store: bool = True):
         import torch
 
         self.torch = torch
         self.wl = wl
         self.step = wl.steps[-1]
+        self.fused_store = fused_store
         dev = "cuda:0"
 
         def up(a):
@@ -202,16 +203,23 @@ class GpuWorkload:
         self.ws = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
 
     def run(self, layer: int, ev=None):
-        """One step on layer `layer`'s pool; ev = (e0, e1, e2, e3) events around metadata, store, attention."""
+        """One step on layer `layer`'s pool; ev = (e0, e1, e2, e3) events around metadata, store, attention (with
+        the fused launch, e0..e1 spans metadata and store, and e1..e2 is empty)."""
         pa, wl, st = self.pa, self.wl, self.step
         kc, vc = self.k_layers[layer], self.v_layers[layer]
         if ev:
             ev[0].record()
-        meta = pa.build_metadata(self.num_cached, self.num_new, self.block_table, self.total_q, wl.num_blocks,
-                                 wl.block_size)
-        if ev:
-            ev[1].record()
-        pa.store_kvcache(self.k, self.v, kc, vc, meta["slot_mapping"])
+        if self.fused_store:
+            meta = pa.build_metadata_store(self.num_cached, self.num_new, self.block_table, self.total_q, self.k,
+                                           self.v, kc, vc)
+            if ev:
+                ev[1].record()
+        else:
+            meta = pa.build_metadata(self.num_cached, self.num_new, self.block_table, self.total_q,
+                                     wl.num_blocks, wl.block_size)
+            if ev:
+                ev[1].record()
+            pa.store_kvcache(self.k, self.v, kc, vc, meta["slot_mapping"])
         if ev:
             ev[2].record()
         if st.kind == "decode":
@@ -464,14 +472,14 @@ def cpu_baseline(wl, budget_s: float):
 # ---------------------------------------------------------------------------------------------- main
 
 
-def bench_one(name: str, steps: int, warmup: int, n_layers: int, out_dtype_name: str):
+def bench_one(name: str, steps: int, warmup: int, n_layers: int, out_dtype_name: str, fused_store: bool = True):
     import torch
 
     from workloads import make_config
 
     wl = make_config(name)
     out_dtype = torch.bfloat16 if out_dtype_name == "bf16" else torch.float32
-    g = GpuWorkload(wl, n_layers, out_dtype)
+    g = GpuWorkload(wl, n_layers, out_dtype, fused_store)
     t = time_workload(g, steps, warmup, n_layers)
     work = algorithmic_work(wl, g.step, 2 if out_dtype == torch.bfloat16 else 4)
     res = {"workload": name, "kind": g.step.kind, "timing": t, "work": work}
@@ -483,10 +491,19 @@ def bench_one(name: str, steps: int, warmup: int, n_layers: int, out_dtype_name:
         res["attn_TFLOPs"] = work["flops"] / (t["attn_ms"] * 1e-3) / 1e12
         res["attn_frac_mfma"] = res["attn_TFLOPs"] / MFMA_BF16_PEAK_TFLOPS
         res["step_TFLOPs"] = work["flops"] / (t["wall_ms_per_step"] * 1e-3) / 1e12
-    res["store_GBps"] = work["store_bytes"] / (t["store_ms"] * 1e-3) / 1e9
+    if fused_store:
+        res["meta_store_GBps"] = (work["store_bytes"] + work["meta_bytes"]) / (t["meta_ms"] * 1e-3) / 1e9
+    else:
+        res["store_GBps"] = work["store_bytes"] / (t["store_ms"] * 1e-3) / 1e9
     del g
     torch.cuda.empty_cache()
     return wl, res
+
+
+def _store_rate(r) -> dict:
+    if "store_GBps" in r:
+        return {"store_GBps": round(r["store_GBps"], 1)}
+    return {"metadata_store_GBps": round(r["meta_store_GBps"], 1)}
 
 
 def main() -> int:
@@ -509,6 +526,9 @@ def main() -> int:
                     help="only time the sampler at the Qwen3 vocabulary for batch 1, 64, 256")
     ap.add_argument("--graph-ladder", action="store_true",
                     help="only time a decode step eager vs captured in a HIP graph over batch sizes 1..256")
+    ap.add_argument("--separate-store", action="store_true",
+                    help="metadata and store as two launches (pa_build_metadata, pa_store_kvcache) instead of one "
+                         "(pa_build_metadata_store)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 1 GiB copy kernel (reference for the HBM byte counters)")
     args = ap.parse_args()
@@ -534,17 +554,19 @@ def main() -> int:
         print(json.dumps({"graph_ladder": graph_ladder([1, 2, 4, 8, 16, 32, 64, 128, 256])}))
         return 0
     main_name = args.only or "decode_qwen3_0p6b"
-    wl, main = bench_one(main_name, args.steps, args.warmup, args.layers, args.out_dtype)
+    fused = not args.separate_store
+    wl, main = bench_one(main_name, args.steps, args.warmup, args.layers, args.out_dtype, fused)
     print(f"[bench] {main_name}: {json.dumps(main['timing'])}", file=sys.stderr, flush=True)
     secondary = []
     if not args.only and not args.no_secondary:
         for name in ("prefill_qwen3_8b", "chunked_qwen3_8b", "decode_qwen3_32b"):
             layers = 1 if name == "decode_qwen3_32b" else args.layers
-            _, r = bench_one(name, max(5, args.steps // 5), max(2, args.warmup // 2), layers, args.out_dtype)
+            _, r = bench_one(name, max(5, args.steps // 5), max(2, args.warmup // 2), layers, args.out_dtype,
+                             fused)
             print(f"[bench] {name}: {json.dumps(r['timing'])}", file=sys.stderr, flush=True)
             entry = {"workload": name, "attn_ms": round(r["timing"]["attn_ms"], 4),
-                     "step_ms": round(r["timing"]["wall_ms_per_step"], 4),
-                     "store_GBps": round(r["store_GBps"], 1)}
+                     "step_ms": round(r["timing"]["wall_ms_per_step"], 4)}
+            entry.update(_store_rate(r))
             if r["kind"] == "decode":
                 entry.update({"attn_GBps": round(r["attn_GBps"], 1), "frac_hbm": round(r["attn_frac_hbm"], 4),
                               "kv_bytes": r["work"]["kv_bytes"]})
@@ -588,11 +610,13 @@ def main() -> int:
                    "num_kv_heads": wl.num_kv_heads, "head_dim": wl.head_dim, "block_size": wl.block_size,
                    "sum_context": work["sum_k"], "new_tokens": work["tokens"], "seed": wl.seed,
                    "out_dtype": args.out_dtype, "layers_cycled": args.layers,
-                   "step": "metadata + store_kvcache + " + ("decode (balanced pass + merge)" if is_dec else "prefill")},
-        "breakdown_ms": {"metadata": round(t["meta_ms"], 5), "store": round(t["store_ms"], 5),
-                         "attention": round(t["attn_ms"], 5), "attention_median": round(t["attn_ms_median"], 5),
+                   "step": ("metadata and store_kvcache in one launch + " if fused else "metadata + store_kvcache + ")
+                   + ("decode (balanced pass + merge)" if is_dec else "prefill")},
+        "breakdown_ms": ({"metadata_store": round(t["meta_ms"], 5)} if fused else
+                         {"metadata": round(t["meta_ms"], 5), "store": round(t["store_ms"], 5)}) |
+                        {"attention": round(t["attn_ms"], 5), "attention_median": round(t["attn_ms_median"], 5),
                          "events_step": round(t["step_ms"], 5)},
-        "store_GBps": round(main["store_GBps"], 1),
+        **_store_rate(main),
         "roofline": roof,
     }
     if not args.no_cpu_baseline:

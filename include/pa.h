@@ -103,6 +103,26 @@ pa_status pa_store_kvcache(const void* k, int64_t k_tok_stride, const void* v, i
                            pa_dtype dtype, void* stream);
 
 /*
+ * pa_build_metadata_store -- pa_build_metadata followed by pa_store_kvcache with its slot_mapping, in one launch.
+ *
+ * Computes every output of pa_build_metadata (same arguments, meanings and limits) and writes each new token's
+ * K and V rows to the slot it computed, exactly as pa_store_kvcache would (bit copy, negative slots skipped). The
+ * two steps run in this order at the start of every step of the engine ("一个 prompt 的一生" §3.3.2 and §4:
+ * prepare the metadata, then each layer's store by slot_mapping); one launch saves the second launch and the wait
+ * between them when the new K/V rows are already at hand. Token t's rows are k[t], v[t] in the flattened order of
+ * the new tokens (sequence by sequence).
+ *   k, v, k_tok_stride, v_tok_stride, k_cache, v_cache, num_kv_heads, head_dim, dtype as for pa_store_kvcache;
+ *   they may be NULL when total_q == 0.
+ */
+pa_status pa_build_metadata_store(const int32_t* num_cached, const int32_t* num_new, const int32_t* block_table,
+                                  int32_t max_blocks_per_seq, int32_t batch, int32_t total_q, int32_t num_blocks,
+                                  int32_t block_size, int32_t* cu_seqlens_q, int32_t* cu_seqlens_k,
+                                  int32_t* context_lens, int32_t* positions, int32_t* slot_mapping, const void* k,
+                                  int64_t k_tok_stride, const void* v, int64_t v_tok_stride, void* k_cache,
+                                  void* v_cache, int32_t num_kv_heads, int32_t head_dim, pa_dtype dtype,
+                                  void* stream);
+
+/*
  * pa_norm_rope_store_kvcache -- the layer's pre-attention step for the new tokens in one pass: k_norm, rotary
  * embedding and the store of K (and V) into the cache, plus q_norm and rotary embedding of Q when q is given.
  *

@@ -8,6 +8,7 @@ The Python functions below only marshal torch tensors into the C calls; see bind
 from .binding import (  # noqa: F401
     PAError,
     build_metadata,
+    build_metadata_store,
     decode,
     decode_split_tokens,
     decode_workspace_bytes,
@@ -22,7 +23,7 @@ from .binding import (  # noqa: F401
 )
 
 __all__ = [
-    "PAError", "build_metadata", "decode", "decode_split_tokens", "decode_workspace_bytes", "lib",
-    "norm_rope_store_kvcache", "sample", "sample_workspace_bytes",
+    "PAError", "build_metadata", "build_metadata_store", "decode", "decode_split_tokens", "decode_workspace_bytes",
+    "lib", "norm_rope_store_kvcache", "sample", "sample_workspace_bytes",
     "prefill_varlen", "prefill_workspace_bytes", "status_str", "store_kvcache",
 ]

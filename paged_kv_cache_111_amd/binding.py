@@ -33,6 +33,9 @@ SIGNATURES = {
                                          _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr]),
     "pa_store_kvcache": (ctypes.c_int, [_c_ptr, _c_i64, _c_ptr, _c_i64, _c_ptr, _c_ptr, _c_ptr, _c_i32, _c_i32,
                                         _c_i32, _c_i32, _c_i32, ctypes.c_int, _c_ptr]),
+    "pa_build_metadata_store": (ctypes.c_int, [_c_ptr, _c_ptr, _c_ptr, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32,
+                                               _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_i64, _c_ptr,
+                                               _c_i64, _c_ptr, _c_ptr, _c_i32, _c_i32, ctypes.c_int, _c_ptr]),
     "pa_norm_rope_store_kvcache": (ctypes.c_int, [_c_ptr, _c_i64, _c_ptr, _c_i64, _c_ptr, _c_ptr, _c_i64, _c_ptr,
                                                   _c_ptr, _c_i32, _c_f32, _c_ptr, _c_ptr, _c_i32, _c_ptr, _c_ptr,
                                                   _c_ptr, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, ctypes.c_int,
@@ -161,6 +164,35 @@ def store_kvcache(k, v, k_cache, v_cache, slot_mapping, stream=None) -> None:
     st = lib().pa_store_kvcache(_ptr(k), ks, _ptr(v), vs, _ptr(k_cache), _ptr(v_cache), _ptr(slot_mapping), T, hkv,
                                 d, nb, bs, _dtype_code(k_cache.dtype), _stream(stream))
     _check("pa_store_kvcache", st)
+
+
+def build_metadata_store(num_cached, num_new, block_table, total_q: int, k, v, k_cache, v_cache,
+                         stream=None) -> dict:
+    """pa_build_metadata_store: build_metadata's outputs (returned as a dict), and k/v [total_q, Hkv, D] stored at
+    the slots it computes."""
+    for t, n in ((num_cached, "num_cached"), (num_new, "num_new"), (block_table, "block_table")):
+        _i32(t, n)
+    nb, bs, hkv, d = _cache_dims(k_cache, v_cache)
+    _require(k.dtype == k_cache.dtype and v.dtype == k_cache.dtype, "k/v must match the cache dtype")
+    ks = _token_rows(k, hkv, d, "k")
+    vs = _token_rows(v, hkv, d, "v")
+    _require(k.shape[0] == total_q and v.shape[0] == total_q, "k and v must have one row per new token")
+    B = int(num_new.shape[0])
+    dev = num_new.device
+    out = {
+        "cu_seqlens_q": torch.empty(B + 1, dtype=torch.int32, device=dev),
+        "cu_seqlens_k": torch.empty(B + 1, dtype=torch.int32, device=dev),
+        "context_lens": torch.empty(B, dtype=torch.int32, device=dev),
+        "positions": torch.empty(max(total_q, 1), dtype=torch.int32, device=dev)[:total_q],
+        "slot_mapping": torch.empty(max(total_q, 1), dtype=torch.int32, device=dev)[:total_q],
+    }
+    st = lib().pa_build_metadata_store(_ptr(num_cached), _ptr(num_new), _ptr(block_table),
+                                       int(block_table.shape[1]), B, int(total_q), nb, bs, _ptr(out["cu_seqlens_q"]),
+                                       _ptr(out["cu_seqlens_k"]), _ptr(out["context_lens"]), _ptr(out["positions"]),
+                                       _ptr(out["slot_mapping"]), _ptr(k), ks, _ptr(v), vs, _ptr(k_cache),
+                                       _ptr(v_cache), hkv, d, _dtype_code(k_cache.dtype), _stream(stream))
+    _check("pa_build_metadata_store", st)
+    return out
 
 
 def norm_rope_store_kvcache(k, v, k_cache, v_cache, slot_mapping, k_norm_weight, positions, cos_sin,

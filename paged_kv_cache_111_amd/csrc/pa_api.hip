@@ -18,6 +18,17 @@ bool valid_head_dim(int32_t d) { return d > 0 && d <= 256 && d % 8 == 0; }
 
 pa_status launched() { return hipGetLastError() == hipSuccess ? PA_OK : PA_ERR_LAUNCH; }
 
+// Widest access (16, 8, 4 or 2 bytes, at least the element size) that every row start and the row length allow
+// for a K/V row copy; 0 when even the element size does not (misaligned element pointers).
+int store_vec(const void* k, int64_t k_stride_bytes, const void* v, int64_t v_stride_bytes, const void* k_cache,
+              const void* v_cache, int64_t row_bytes, int elem) {
+  for (int vec = 16; vec >= elem; vec >>= 1)
+    if (row_bytes % vec == 0 && k_stride_bytes % vec == 0 && v_stride_bytes % vec == 0 && aligned(k, vec) &&
+        aligned(v, vec) && aligned(k_cache, vec) && aligned(v_cache, vec))
+      return vec;
+  return 0;
+}
+
 // Keys per decode split chosen from host sizes only: about 32k work items for contexts at half the table's
 // capacity, clamped to [256, 4096] keys and rounded to a power of two (a multiple of 32).
 int32_t auto_split(int32_t batch, int32_t num_kv_heads, int32_t mbps, int32_t block_size) {
@@ -106,16 +117,42 @@ pa_status pa_store_kvcache(const void* k, int64_t k_tok_stride, const void* v, i
   if (num_tokens == 0) return PA_OK;
   if (!k || !v || !k_cache || !v_cache || !slot_mapping) return PA_ERR_NULL;
   const int eb = elem_bytes(dtype);
-  const int64_t row_bytes = row * eb;
-  const int64_t ksb = k_tok_stride * eb, vsb = v_tok_stride * eb;
-  int vec = 16;
-  while (vec > eb && (row_bytes % vec || ksb % vec || vsb % vec || !aligned(k, vec) || !aligned(v, vec) ||
-                      !aligned(k_cache, vec) || !aligned(v_cache, vec)))
-    vec >>= 1;
-  if (row_bytes % vec || !aligned(k, vec) || !aligned(v, vec) || !aligned(k_cache, vec) || !aligned(v_cache, vec))
-    return PA_ERR_SHAPE;  // misaligned element pointers
-  pa::launch_store_kvcache(k, ksb, v, vsb, k_cache, v_cache, slot_mapping, num_tokens, row_bytes, vec,
-                           static_cast<hipStream_t>(stream));
+  const int vec = store_vec(k, k_tok_stride * eb, v, v_tok_stride * eb, k_cache, v_cache, row * eb, eb);
+  if (!vec) return PA_ERR_SHAPE;  // misaligned element pointers
+  pa::launch_store_kvcache(k, k_tok_stride * eb, v, v_tok_stride * eb, k_cache, v_cache, slot_mapping, num_tokens,
+                           row * eb, vec, static_cast<hipStream_t>(stream));
+  return launched();
+}
+
+pa_status pa_build_metadata_store(const int32_t* num_cached, const int32_t* num_new, const int32_t* block_table,
+                                  int32_t max_blocks_per_seq, int32_t batch, int32_t total_q, int32_t num_blocks,
+                                  int32_t block_size, int32_t* cu_seqlens_q, int32_t* cu_seqlens_k,
+                                  int32_t* context_lens, int32_t* positions, int32_t* slot_mapping, const void* k,
+                                  int64_t k_tok_stride, const void* v, int64_t v_tok_stride, void* k_cache,
+                                  void* v_cache, int32_t num_kv_heads, int32_t head_dim, pa_dtype dtype,
+                                  void* stream) {
+  if (!valid_dtype(dtype)) return PA_ERR_UNSUPPORTED;
+  if (batch < 0 || batch > 4096 || total_q < 0 || block_size <= 0 || num_blocks <= 0 || num_kv_heads <= 0 ||
+      head_dim <= 0)
+    return PA_ERR_SHAPE;
+  if (int64_t(num_blocks) * block_size > kInt32Max) return PA_ERR_SHAPE;
+  const int64_t row = int64_t(num_kv_heads) * head_dim;
+  if (k_tok_stride < row || v_tok_stride < row) return PA_ERR_SHAPE;
+  if (batch == 0) return total_q == 0 ? PA_OK : PA_ERR_SHAPE;
+  if (max_blocks_per_seq <= 0) return PA_ERR_SHAPE;
+  if (!num_cached || !num_new || !block_table || !cu_seqlens_q || !cu_seqlens_k || !context_lens)
+    return PA_ERR_NULL;
+  if (total_q > 0 && (!positions || !slot_mapping || !k || !v || !k_cache || !v_cache)) return PA_ERR_NULL;
+  const int eb = elem_bytes(dtype);
+  int vec = eb;
+  if (total_q > 0) {
+    vec = store_vec(k, k_tok_stride * eb, v, v_tok_stride * eb, k_cache, v_cache, row * eb, eb);
+    if (!vec) return PA_ERR_SHAPE;
+  }
+  pa::launch_metadata_store(num_cached, num_new, block_table, max_blocks_per_seq, batch, total_q, block_size,
+                            cu_seqlens_q, cu_seqlens_k, context_lens, positions, slot_mapping, k, k_tok_stride * eb,
+                            v, v_tok_stride * eb, k_cache, v_cache, row * eb, vec,
+                            static_cast<hipStream_t>(stream));
   return launched();
 }
 

@@ -9,6 +9,12 @@ void launch_build_metadata(const int32_t* num_cached, const int32_t* num_new, co
                            int32_t mbps, int32_t batch, int32_t total_q, int32_t block_size, int32_t* cu_q,
                            int32_t* cu_k, int32_t* ctx, int32_t* pos, int32_t* slot, hipStream_t stream);
 
+void launch_metadata_store(const int32_t* num_cached, const int32_t* num_new, const int32_t* block_table,
+                           int32_t mbps, int32_t batch, int32_t total_q, int32_t block_size, int32_t* cu_q,
+                           int32_t* cu_k, int32_t* ctx, int32_t* pos, int32_t* slot, const void* k,
+                           int64_t k_stride_bytes, const void* v, int64_t v_stride_bytes, void* k_cache,
+                           void* v_cache, int64_t row_bytes, int vec_bytes, hipStream_t stream);
+
 void launch_store_kvcache(const void* k, int64_t k_stride_bytes, const void* v, int64_t v_stride_bytes,
                           void* k_cache, void* v_cache, const int32_t* slot_mapping, int32_t num_tokens,
                           int64_t row_bytes, int vec_bytes, hipStream_t stream);

@@ -16,16 +16,13 @@ namespace pa {
 // context_lens.
 constexpr int kMetaThreads = 256;
 
-__global__ __launch_bounds__(kMetaThreads) void build_metadata_kernel(
-    const int32_t* __restrict__ num_cached, const int32_t* __restrict__ num_new,
-    const int32_t* __restrict__ block_table, int32_t mbps, int32_t batch, int32_t total_q, int32_t block_size,
-    int32_t* __restrict__ cu_q_out, int32_t* __restrict__ cu_k_out, int32_t* __restrict__ ctx_out,
-    int32_t* __restrict__ pos_out, int32_t* __restrict__ slot_out) {
-  extern __shared__ int32_t smem[];
-  int32_t* cu_q = smem;                  // [batch + 1]
-  int32_t* cu_k = smem + (batch + 1);    // [batch + 1]
-  __shared__ int32_t wave_q[kMetaThreads / 64], wave_k[kMetaThreads / 64];
-
+// Fills cu_q[0..batch] and cu_k[0..batch] (LDS) with the prefix sums of num_new and of num_cached + num_new;
+// workgroup 0 also writes them, and context_lens, to global memory. Called by all kMetaThreads threads.
+__device__ __forceinline__ void meta_prefix_sums(const int32_t* __restrict__ num_cached,
+                                                 const int32_t* __restrict__ num_new, int32_t batch,
+                                                 int32_t* cu_q, int32_t* cu_k, int32_t* wave_q, int32_t* wave_k,
+                                                 int32_t* __restrict__ cu_q_out, int32_t* __restrict__ cu_k_out,
+                                                 int32_t* __restrict__ ctx_out) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
@@ -79,19 +76,132 @@ __global__ __launch_bounds__(kMetaThreads) void build_metadata_kernel(
       cu_k_out[s] = cu_k[s];
     }
   }
-  const int t = blockIdx.x * kMetaThreads + tid;
-  if (t >= total_q) return;
-  // largest s with cu_q[s] <= t (sequences with no new tokens have cu_q[s] == cu_q[s+1] and are skipped)
+}
+
+// Sequence of new token t (the largest s with cu_q[s] <= t: sequences with no new tokens have
+// cu_q[s] == cu_q[s + 1] and are skipped), its absolute position and its slot.
+__device__ __forceinline__ int32_t meta_token(int32_t t, const int32_t* cu_q, int32_t batch,
+                                              const int32_t* __restrict__ num_cached,
+                                              const int32_t* __restrict__ block_table, int32_t mbps,
+                                              int32_t block_size, int32_t& pos) {
   int a = 0, b = batch;  // invariant: cu_q[a] <= t < cu_q[b]
   while (b - a > 1) {
     const int mid = (a + b) >> 1;
     if (cu_q[mid] <= t) a = mid; else b = mid;
   }
-  const int32_t pos = num_cached[a] + (t - cu_q[a]);
+  pos = num_cached[a] + (t - cu_q[a]);
   const int32_t blk = pos / block_size;
-  const int32_t phys = block_table[int64_t(a) * mbps + blk];
+  return block_table[int64_t(a) * mbps + blk] * block_size + (pos - blk * block_size);
+}
+
+__global__ __launch_bounds__(kMetaThreads) void build_metadata_kernel(
+    const int32_t* __restrict__ num_cached, const int32_t* __restrict__ num_new,
+    const int32_t* __restrict__ block_table, int32_t mbps, int32_t batch, int32_t total_q, int32_t block_size,
+    int32_t* __restrict__ cu_q_out, int32_t* __restrict__ cu_k_out, int32_t* __restrict__ ctx_out,
+    int32_t* __restrict__ pos_out, int32_t* __restrict__ slot_out) {
+  extern __shared__ int32_t smem[];
+  __shared__ int32_t wave_q[kMetaThreads / 64], wave_k[kMetaThreads / 64];
+  int32_t* cu_q = smem;                  // [batch + 1]
+  int32_t* cu_k = smem + (batch + 1);    // [batch + 1]
+  meta_prefix_sums(num_cached, num_new, batch, cu_q, cu_k, wave_q, wave_k, cu_q_out, cu_k_out, ctx_out);
+  const int t = blockIdx.x * kMetaThreads + threadIdx.x;
+  if (t >= total_q) return;
+  int32_t pos;
+  const int32_t slot = meta_token(t, cu_q, batch, num_cached, block_table, mbps, block_size, pos);
   pos_out[t] = pos;
-  slot_out[t] = phys * block_size + (pos - blk * block_size);
+  slot_out[t] = slot;
+}
+
+// ------------------------------------------------------------------------------------------------- both
+//
+// Metadata and store in one launch: one wave per new token, four per workgroup (each workgroup rebuilds the
+// prefix sums as above). The wave issues the loads of its token's K and V rows first, since they depend on the
+// token index alone, so that they are in flight during the prefix sums; it then finds the token's slot, writes
+// the position and the slot, and writes the rows to the slot (no write for a negative slot).
+template <typename VecT>
+__global__ __launch_bounds__(kMetaThreads) void metadata_store_kernel(
+    const int32_t* __restrict__ num_cached, const int32_t* __restrict__ num_new,
+    const int32_t* __restrict__ block_table, int32_t mbps, int32_t batch, int32_t total_q, int32_t block_size,
+    int32_t* __restrict__ cu_q_out, int32_t* __restrict__ cu_k_out, int32_t* __restrict__ ctx_out,
+    int32_t* __restrict__ pos_out, int32_t* __restrict__ slot_out, const char* __restrict__ k,
+    int64_t k_stride_bytes, const char* __restrict__ v, int64_t v_stride_bytes, char* __restrict__ k_cache,
+    char* __restrict__ v_cache, int32_t row_vecs) {
+  extern __shared__ int32_t smem[];
+  __shared__ int32_t wave_q[kMetaThreads / 64], wave_k[kMetaThreads / 64];
+  int32_t* cu_q = smem;                  // [batch + 1]
+  int32_t* cu_k = smem + (batch + 1);    // [batch + 1]
+  constexpr int kRegVecs = 4;            // rows of up to 4 * 64 vectors are held in registers meanwhile
+
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * (kMetaThreads / 64) + (threadIdx.x >> 6);
+  const bool has_token = t < total_q;
+  const bool in_regs = row_vecs <= kRegVecs * 64;
+  const VecT* ks = reinterpret_cast<const VecT*>(k + int64_t(t) * k_stride_bytes);
+  const VecT* vs = reinterpret_cast<const VecT*>(v + int64_t(t) * v_stride_bytes);
+  VecT kr[kRegVecs] = {}, vr[kRegVecs] = {};
+  if (has_token && in_regs) {
+#pragma unroll
+    for (int j = 0; j < kRegVecs; ++j) {
+      const int i = lane + 64 * j;
+      if (i < row_vecs) {
+        kr[j] = ks[i];
+        vr[j] = vs[i];
+      }
+    }
+  }
+  meta_prefix_sums(num_cached, num_new, batch, cu_q, cu_k, wave_q, wave_k, cu_q_out, cu_k_out, ctx_out);
+  if (!has_token) return;
+  int32_t pos;
+  const int32_t slot = meta_token(t, cu_q, batch, num_cached, block_table, mbps, block_size, pos);
+  if (lane == 0) {
+    pos_out[t] = pos;
+    slot_out[t] = slot;
+  }
+  if (slot < 0) return;
+  const int64_t row_bytes = int64_t(row_vecs) * sizeof(VecT);
+  VecT* kd = reinterpret_cast<VecT*>(k_cache + int64_t(slot) * row_bytes);
+  VecT* vd = reinterpret_cast<VecT*>(v_cache + int64_t(slot) * row_bytes);
+  if (in_regs) {
+#pragma unroll
+    for (int j = 0; j < kRegVecs; ++j) {
+      const int i = lane + 64 * j;
+      if (i < row_vecs) {
+        kd[i] = kr[j];
+        vd[i] = vr[j];
+      }
+    }
+  } else {
+    for (int i = lane; i < row_vecs; i += 64) {
+      const VecT a = ks[i];
+      const VecT b = vs[i];
+      kd[i] = a;
+      vd[i] = b;
+    }
+  }
+}
+
+void launch_metadata_store(const int32_t* num_cached, const int32_t* num_new, const int32_t* block_table,
+                           int32_t mbps, int32_t batch, int32_t total_q, int32_t block_size, int32_t* cu_q,
+                           int32_t* cu_k, int32_t* ctx, int32_t* pos, int32_t* slot, const void* k,
+                           int64_t k_stride_bytes, const void* v, int64_t v_stride_bytes, void* k_cache,
+                           void* v_cache, int64_t row_bytes, int vec_bytes, hipStream_t stream) {
+  const int grid = total_q > 0 ? (total_q + kMetaThreads / 64 - 1) / (kMetaThreads / 64) : 1;
+  const size_t lds = size_t(2) * (batch + 1) * sizeof(int32_t);
+  const char* kp = static_cast<const char*>(k);
+  const char* vp = static_cast<const char*>(v);
+  char* kc = static_cast<char*>(k_cache);
+  char* vc = static_cast<char*>(v_cache);
+#define PA_LAUNCH_MS(VT)                                                                                        \
+  hipLaunchKernelGGL(metadata_store_kernel<VT>, dim3(grid), dim3(kMetaThreads), lds, stream, num_cached, num_new, \
+                     block_table, mbps, batch, total_q, block_size, cu_q, cu_k, ctx, pos, slot, kp,              \
+                     k_stride_bytes, vp, v_stride_bytes, kc, vc, int32_t(row_bytes / sizeof(VT)))
+  switch (vec_bytes) {
+    case 16: PA_LAUNCH_MS(u32x4); break;
+    case 8: PA_LAUNCH_MS(u32x2); break;
+    case 4: PA_LAUNCH_MS(uint32_t); break;
+    default: PA_LAUNCH_MS(uint16_t); break;
+  }
+#undef PA_LAUNCH_MS
 }
 
 void launch_build_metadata(const int32_t* num_cached, const int32_t* num_new, const int32_t* block_table,

@@ -52,10 +52,16 @@ class DevStep:
         self.max_k = int((step.num_cached + step.num_new).max()) if step.batch else 0
 
 
-def hip_step(wl, ds: DevStep, kc: torch.Tensor, vc: torch.Tensor, out_dtype=torch.float32, split_tokens=0):
-    """The whole path on the GPU: metadata, store, attention. Returns (metadata tensors, output tensor)."""
-    meta = pa.build_metadata(ds.num_cached, ds.num_new, ds.block_table, ds.total_q, wl.num_blocks, wl.block_size)
-    pa.store_kvcache(ds.k, ds.v, kc, vc, meta["slot_mapping"])
+def hip_step(wl, ds: DevStep, kc: torch.Tensor, vc: torch.Tensor, out_dtype=torch.float32, split_tokens=0,
+             fused_store=False):
+    """The whole path on the GPU: metadata, store, attention (metadata and store in one launch with fused_store).
+    Returns (metadata tensors, output tensor)."""
+    if fused_store:
+        meta = pa.build_metadata_store(ds.num_cached, ds.num_new, ds.block_table, ds.total_q, ds.k, ds.v, kc, vc)
+    else:
+        meta = pa.build_metadata(ds.num_cached, ds.num_new, ds.block_table, ds.total_q, wl.num_blocks,
+                                 wl.block_size)
+        pa.store_kvcache(ds.k, ds.v, kc, vc, meta["slot_mapping"])
     if ds.step.kind == "prefill":
         out = pa.prefill_varlen(ds.q, kc, vc, meta["cu_seqlens_q"], meta["cu_seqlens_k"], ds.block_table, ds.max_q,
                                 ds.max_k, wl.scale, out_dtype=out_dtype)

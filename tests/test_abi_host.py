@@ -67,6 +67,29 @@ def test_metadata_rejects_bad_arguments():
     assert lib.pa_build_metadata(z, z, z, 4, 2, 5, 16, 0, z, z, z, z, z, z) == b.PA_ERR_SHAPE
 
 
+def _meta_store(**kw):
+    args = dict(nc=NULL, nn=NULL, bt=NULL, mbps=4, batch=2, total_q=5, nb=16, bs=4, cq=NULL, ck=NULL, ctx=NULL,
+                pos=NULL, slot=NULL, k=NULL, ks=1024, v=NULL, vs=1024, kc=NULL, vc=NULL, hkv=8, d=128, dtype=1,
+                st=NULL)
+    args.update(kw)
+    return pa.lib().pa_build_metadata_store(*args.values())
+
+
+def test_metadata_store_rejects_bad_arguments():
+    fake = 0x10000  # never dereferenced: every call below returns before a launch
+    dev = dict(nc=fake, nn=fake, bt=fake, cq=fake, ck=fake, ctx=fake, pos=fake, slot=fake)
+    assert _meta_store() == b.PA_ERR_NULL
+    assert _meta_store(batch=0, total_q=0) == b.PA_OK
+    assert _meta_store(batch=0, total_q=3) == b.PA_ERR_SHAPE
+    assert _meta_store(batch=5000) == b.PA_ERR_SHAPE
+    assert _meta_store(bs=0) == b.PA_ERR_SHAPE
+    assert _meta_store(ks=100) == b.PA_ERR_SHAPE                     # token stride shorter than a row
+    assert _meta_store(dtype=7) == b.PA_ERR_UNSUPPORTED
+    assert _meta_store(nb=2 ** 24, bs=256) == b.PA_ERR_SHAPE          # slots beyond int32
+    assert _meta_store(**dev) == b.PA_ERR_NULL                        # new tokens but no K/V or caches
+    assert _meta_store(**dev, k=fake + 1, v=fake, kc=fake, vc=fake) == b.PA_ERR_SHAPE  # misaligned bf16 row
+
+
 def _prefill(**kw):
     args = dict(q=NULL, qs=32 * 128, kc=NULL, vc=NULL, cq=NULL, ck=NULL, bt=NULL, mbps=8, batch=2, total_q=10,
                 msq=8, msk=8, hq=32, hkv=8, d=128, nb=16, bs=256, scale=0.1, dtype=1, out=NULL, odt=0, ws=NULL,

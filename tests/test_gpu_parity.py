@@ -17,7 +17,8 @@ from workloads import build_decode, build_prefill, make_config
 pytestmark = pytest.mark.gpu
 
 
-def _run_and_check(wl, out_dtype=torch.float32, split_tokens=0, seqs=None, rows=None, check_pool=True):
+def _run_and_check(wl, out_dtype=torch.float32, split_tokens=0, seqs=None, rows=None, check_pool=True,
+                   fused_store=False):
     """Every step of the workload on both sides; returns the per-step (max_abs, rel_rms)."""
     kc_h, vc_h = wl.k_cache.copy(), wl.v_cache.copy()
     kc, vc = to_dev(wl.k_cache, wl.dtype), to_dev(wl.v_cache, wl.dtype)
@@ -25,7 +26,8 @@ def _run_and_check(wl, out_dtype=torch.float32, split_tokens=0, seqs=None, rows=
     for i, step in enumerate(wl.steps):
         print(f"[case] {wl.name} step {i} {step.kind} B={step.batch} T={step.num_tokens}", flush=True)
         ds = DevStep(step, wl.dtype)
-        meta_d, out = hip_step(wl, ds, kc, vc, out_dtype=out_dtype, split_tokens=split_tokens)
+        meta_d, out = hip_step(wl, ds, kc, vc, out_dtype=out_dtype, split_tokens=split_tokens,
+                               fused_store=fused_store)
         torch.cuda.synchronize()
         meta_r, ref = oracle_step(wl, step, kc_h, vc_h, seqs=seqs, rows=rows)
         compare_metadata(meta_d, meta_r)
@@ -181,6 +183,70 @@ def test_decode_largest_batch():
     ctx = [int(x) for x in np.random.default_rng(11).integers(1, 65, 4096)]
     wl = build_decode("decode_4096", 620, 8, 2, 128, 32, "bf16", ctx, num_blocks=sum(-(-n // 32) for n in ctx) + 2)
     _run_and_check(wl)
+
+
+# metadata and store in one launch (pa_build_metadata_store) on shapes of the cases above: bf16 and f32 rows of
+# 64 to 4096 bytes, block sizes 1 to 256, sequences without new tokens, 300 and 4096 sequences
+FUSED_STORE_CASES = [("prefill", 0), ("prefill", 4), ("prefill", 5), ("prefill", 6), ("prefill", 10),
+                     ("decode", 0), ("decode", 9), ("decode", 11)]
+
+
+@pytest.mark.parametrize("case", FUSED_STORE_CASES)
+def test_fused_metadata_store(case):
+    kind, i = case
+    if kind == "prefill":
+        Hq, Hkv, D, bs, dt, kl, cached = PREFILL_CASES[i]
+        wl = build_prefill(f"fused_prefill_{i}", 200 + i, Hq, Hkv, D, bs, dt, kl, cached,
+                           num_blocks=sum(-(-n // bs) for n in kl) + 3)
+    else:
+        Hq, Hkv, D, bs, dt, ctx, _ = DECODE_CASES[i]
+        wl = build_decode(f"fused_decode_{i}", 300 + i, Hq, Hkv, D, bs, dt, ctx,
+                          num_blocks=sum(-(-n // bs) for n in ctx) + 2)
+    _run_and_check(wl, fused_store=True)
+
+
+def test_fused_metadata_store_empty_sequences_and_large_batch():
+    kl, cached = [40, 33, 70, 16], [40, 5, 70, 0]
+    wl = build_prefill("fused_prefill_empty", 626, 8, 2, 128, 16, "bf16", kl, cached,
+                       num_blocks=sum(-(-n // 16) for n in kl) + 2, allow_empty=True)
+    _run_and_check(wl, fused_store=True)
+    ctx = [int(x) for x in np.random.default_rng(11).integers(1, 65, 4096)]
+    wl = build_decode("fused_decode_4096", 620, 8, 2, 128, 32, "bf16", ctx,
+                      num_blocks=sum(-(-n // 32) for n in ctx) + 2)
+    _run_and_check(wl, fused_store=True)
+
+
+@pytest.mark.parametrize("hkv, stride_pad", [(32, 0), (8, 1)])
+def test_fused_metadata_store_wide_and_unaligned_rows(hkv, stride_pad):
+    """Rows of 8 KiB (past what the kernel keeps in registers) and rows whose token stride is odd (2-byte copies),
+    as views of a fused projection output; metadata and cache bit-exact against the oracle."""
+    D, bs, hq = 128, 16, 8
+    rng = np.random.default_rng(40 + hkv)
+    cached = np.array([3, 0, 17, 40], np.int64)
+    new = np.array([5, 12, 1, 0], np.int64)
+    nbk = [-(-int(c + n) // bs) for c, n in zip(cached, new)]
+    nb = sum(nbk) + 4
+    perm = rng.permutation(nb).astype(np.int32)
+    table = np.full((4, max(nbk)), -1, np.int32)
+    at = 0
+    for s in range(4):
+        table[s, :nbk[s]] = perm[at:at + nbk[s]]
+        at += nbk[s]
+    T = int(new.sum())
+    width = (hq + 2 * hkv) * D + stride_pad
+    qkv = torch.from_numpy(rng.standard_normal((T, width)).astype(np.float32)).to(DEV).bfloat16()
+    k = qkv[:, hq * D:(hq + hkv) * D].view(T, hkv, D)
+    v = qkv[:, (hq + hkv) * D:(hq + 2 * hkv) * D].view(T, hkv, D)
+    kc_h = rng.standard_normal((nb, bs, hkv, D)).astype(np.float32)
+    kc = torch.from_numpy(kc_h).to(DEV).bfloat16()
+    vc = kc.clone()
+    ref_k, ref_v = to_host_bits(kc), to_host_bits(vc)
+    meta = pa.build_metadata_store(i32(cached), i32(new), i32(table), T, k, v, kc, vc)
+    ref = oracle.build_metadata(table, cached, new, bs)
+    compare_metadata(meta, ref)
+    oracle.store_kvcache(ref_k, ref_v, to_host_bits(k.contiguous()), to_host_bits(v.contiguous()),
+                         ref["slot_mapping"])
+    assert np.array_equal(to_host_bits(kc), ref_k) and np.array_equal(to_host_bits(vc), ref_v)
 
 
 def test_bf16_output():
