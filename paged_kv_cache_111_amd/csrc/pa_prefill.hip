@@ -5,8 +5,8 @@
 // tile's global loads are in flight in registers while the current tile is computed), shared by the four waves:
 //   S^T[key, q] = K[key, :] . Q[q, :]      32x32x16 MFMA, A = K rows from LDS, B = Q^T kept in registers
 //   O^T[d, q]  += V^T[d, key] P^T[key, q]  32x32x16 fp16 MFMA, A = V^T via the LDS transpose read (V is
-//                                           converted to fp16 when staged), B = P^T (fp16) kept in the
-//                                           registers the score MFMA left the scores in
+//                                           converted to fp16 when staged), B = P^T (fp16) formed
+//                                           lane by lane from the scores the score MFMA left
 // With scores transposed, each lane owns one query column; its keys are split over the two wave halves, which
 // exchange the row max only when a tile moves the running reference max, and the row sum once at the end.
 // The key -> k-slot assignment of the second product follows the score layout (lane half hh holds keys
@@ -29,30 +29,6 @@
 namespace pa {
 
 constexpr int kPreRows = 128;  // query rows per workgroup
-
-// Scheduling hints (instruction groups in issue order) for the two long blocks of a step; the ratios were
-// chosen by timing (three vector instructions per score MFMA measured best of 1-4).
-// Mask bits: 0x2 VALU, 0x8 MFMA, 0x20 VMEM read, 0x100 DS read, 0x200 DS write.
-__device__ __forceinline__ void pf_sched_scores() {
-  __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
-  }
-}
-__device__ __forceinline__ void pf_sched_weights_pv() {
-  __builtin_amdgcn_sched_group_barrier(0x002, 24, 0);
-  __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-    __builtin_amdgcn_sched_group_barrier(0x002, 8, 0);
-    __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
-  }
-}
 
 template <bool kAligned, bool kPow2>
 __global__ __launch_bounds__(kPreThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_mfma_kernel(
@@ -108,8 +84,8 @@ __global__ __launch_bounds__(kPreThreads) __attribute__((amdgpu_waves_per_eu(2, 
     for (int ks = 0; ks < 8; ++ks) qb[ks] = as_bf16x8(ok ? ld16(qp + 16 * ks) : z);
   }
 
-  // K tiles run one tile ahead of V tiles: while tile j's softmax and PV run, tile j+1's scores are already
-  // being computed (so the matrix cores work during the softmax) and K tile j+2 / V tile j+1 are loading.
+  // K tiles run one tile ahead of V tiles: step j computes tile j+1's scores as well as tile j's softmax and PV
+  // (so a wave's matrix work comes in two blocks per step), while K tile j+2 and V tile j+1 are loading.
   __shared__ __attribute__((aligned(16))) uint16_t kt[2][kPreKeys * kKRow];
   __shared__ __attribute__((aligned(16))) uint16_t vt[2][kPreKeys * kVRow];
 
@@ -150,10 +126,8 @@ __global__ __launch_bounds__(kPreThreads) __attribute__((amdgpu_waves_per_eu(2, 
     pf_gload1<kAligned, kPow2>(vst, vbase, table, kb + kPreKeys, k_len, bs, bs_shift, row_bytes, tid);
     if (j < wave_tiles) {
       if (kb + kPreKeys - 1 > past + wave_row0) pf_mask(cur, my_pos - kb - 4 * hh);
-      // tile j+1's scores on the matrix cores while tile j's row max runs on the vector ALUs
-      pf_scores(nxt, kt[1 - P], ka_off, qb);
       const float mh = pf_halfmax(cur) * scale_log2;
-      pf_sched_scores();
+      pf_scores(nxt, kt[1 - P], ka_off, qb);  // tile j+1's scores (K tile j+1 has been in LDS since the last step)
       // The reference max only moves when the row max would exceed it by more than the slack; until then the
       // weights exp2(s - m) stay below 2^8 and O, l need no rescaling. The result O / l does not depend on m.
       // The row's keys are split over the two wave halves: the vote runs on each half's own max (no half above
@@ -169,7 +143,6 @@ __global__ __launch_bounds__(kPreThreads) __attribute__((amdgpu_waves_per_eu(2, 
       pf_weights_pv(cur, o, m, lsum, vt[P], va_off, scale_log2);
       pf_lstore_k(kst, kt[P], tid);      // K tile j+2 replaces K tile j (scored in the previous step)
       pf_lstore_v(vst, vt[1 - P], tid);  // V tile j+1 replaces V tile j-1 (read by the previous step's PV)
-      pf_sched_weights_pv();
     } else {
       pf_lstore_k(kst, kt[P], tid);
       pf_lstore_v(vst, vt[1 - P], tid);

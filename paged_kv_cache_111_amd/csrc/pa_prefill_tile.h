@@ -3,8 +3,8 @@
 //
 //   S^T[key, q] = K[key, :] . Q[q, :]      32x32x16 MFMA, A = K rows from LDS, B = Q^T kept in registers
 //   O^T[d, q]  += V^T[d, key] P^T[key, q]  32x32x16 fp16 MFMA, A = V^T via the LDS transpose read (V is
-//                                           converted to fp16 when staged), B = P^T (fp16) kept in the
-//                                           registers the score MFMA left the scores in
+//                                           converted to fp16 when staged), B = P^T (fp16) formed
+//                                           lane by lane from the scores the score MFMA left
 // With scores transposed, each lane owns one query column; its keys are split over the two wave halves, which
 // exchange the row max only when a tile moves the running reference max, and the row sum once at the end.
 // The key -> k-slot assignment of the second product follows the score layout (lane half hh holds keys
@@ -16,10 +16,11 @@
 namespace pa {
 
 constexpr int kPreThreads = 256;  // threads that stage one tile (four waves)
-constexpr int kKRow = 128 + 8;    // LDS row stride of the K tile, in elements (272 bytes: 16-byte reads of
-                                  // consecutive rows land 4 banks apart)
-constexpr int kVRow = 128 + 16;   // LDS row stride of the V tile (288 bytes: the transposed 8-byte reads of 4
-                                  // consecutive rows land 8 banks apart; 8 or 24 measured no better)
+constexpr int kKRow = 128 + 8;    // LDS row stride of the K tile, in elements (272 bytes: the 16-byte reads of
+                                  // 16 consecutive rows fall on distinct banks)
+constexpr int kVRow = 128 + 32;   // LDS row stride of the V tile (320 bytes: the transposed 8-byte reads of 32
+                                  // lanes span 4 rows x 64 bytes, which this stride spreads over all 64 banks;
+                                  // 288-byte rows left a quarter of the LDS-active cycles in bank conflicts)
 #ifndef PA_PREFILL_KEYS
 #define PA_PREFILL_KEYS 64
 #endif
@@ -129,9 +130,12 @@ __device__ __forceinline__ float pf_halfmax(const f32x16 (&sc)[kSub]) {
 // product, so the weights the output averages with sum to one) and O^T += V^T P^T from the V tile in LDS.
 // Lane group g4 = lane / 16 (half hh = g4 / 2, d offset 16 (g4 % 2)); for k-step kk the lane's slots 0..3 are
 // keys 16 kk + 4 hh + 0..3 and slots 4..7 keys 16 kk + 8 + 4 hh + 0..3.
+// All weights are formed first and the 16 MFMAs then run back to back: vector instructions placed between one
+// wave's MFMAs stall its issue, while the other wave on the SIMD can run its vector work during them.
 __device__ __forceinline__ void pf_weights_pv(const f32x16 (&sc)[kSub], f32x16 (&o)[4], float m, float& lsum,
                                               const uint16_t* vt, int va_off, float scale_log2) {
   float psum[2] = {0.f, 0.f};  // two independent chains
+  f16x8 pb[kSub][2];
 #pragma unroll
   for (int sub = 0; sub < kSub; ++sub) {
 #pragma unroll
@@ -142,14 +146,20 @@ __device__ __forceinline__ void pf_weights_pv(const f32x16 (&sc)[kSub], f32x16 (
       const u32x4 pw = {pack_f16x2(p[0], p[1]), pack_f16x2(p[2], p[3]), pack_f16x2(p[4], p[5]),
                         pack_f16x2(p[6], p[7])};
       psum[kk] = add_f16x2(pw[3], add_f16x2(pw[2], add_f16x2(pw[1], add_f16x2(pw[0], psum[kk]))));
-      const f16x8 pb = as_f16x8(pw);
+      pb[sub][kk] = as_f16x8(pw);
+    }
+  }
+#pragma unroll
+  for (int sub = 0; sub < kSub; ++sub) {
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
       const uint16_t* vr = vt + va_off + (32 * sub + 16 * kk) * kVRow;
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
         const i16x4 a0 = lds_read_tr16(vr + 32 * mt);
         const i16x4 a1 = lds_read_tr16(vr + 8 * kVRow + 32 * mt);
         const f16x8 av = __builtin_bit_cast(f16x8, __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7));
-        o[mt] = mfma32x32x16_f16(av, pb, o[mt]);
+        o[mt] = mfma32x32x16_f16(av, pb[sub][kk], o[mt]);
       }
     }
   }
