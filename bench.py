@@ -143,7 +143,7 @@ def write_traffic_summary(workload: str, fetch_csv: str, write_csv: str) -> dict
                 "on a plain copy kernel (torch.mul over 1 GiB of fp16: reads 1 GiB, writes 1 GiB)",
         "commands": [f"cd /tmp && rocprofv3 --pmc {c} -d gpurun_out/pmc_{c}_{workload} -o pmc --output-format csv "
                      f"-- python /root/repo/bench.py --only {workload} --no-cpu-baseline --steps 5 --warmup 2 "
-                     f"--calibrate-copy" for c in ("FETCH_SIZE", "WRITE_SIZE")]
+                     f"--prewarm 0 --calibrate-copy" for c in ("FETCH_SIZE", "WRITE_SIZE")]
                     + [f"python bench.py --only {workload} --traffic-summary "
                        f"gpurun_out/pmc_FETCH_SIZE_{workload}/pmc_counter_collection.csv "
                        f"gpurun_out/pmc_WRITE_SIZE_{workload}/pmc_counter_collection.csv"],
@@ -531,6 +531,7 @@ def _store_rate(r) -> dict:
 
 
 def main() -> int:
+    global PREWARM_S
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
@@ -550,12 +551,15 @@ def main() -> int:
                     help="only time the sampler at the Qwen3 vocabulary for batch 1, 64, 256")
     ap.add_argument("--graph-ladder", action="store_true",
                     help="only time a decode step eager vs captured in a HIP graph over batch sizes 1..256")
+    ap.add_argument("--prewarm", type=float, default=PREWARM_S,
+                    help="seconds of untimed steps before the warmup steps (0 for counter runs)")
     ap.add_argument("--separate-store", action="store_true",
                     help="metadata and store as two launches (pa_build_metadata, pa_store_kvcache) instead of one "
                          "(pa_build_metadata_store)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 1 GiB copy kernel (reference for the HBM byte counters)")
     args = ap.parse_args()
+    PREWARM_S = args.prewarm
     if args.traffic_summary:
         if not args.only:
             ap.error("--traffic-summary needs --only WORKLOAD")
