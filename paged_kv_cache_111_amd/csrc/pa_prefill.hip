@@ -177,9 +177,6 @@ __global__ __launch_bounds__(kPreThreads) __attribute__((amdgpu_waves_per_eu(2, 
   }
 }
 
-#ifndef PA_PF_DYN_LDS
-#define PA_PF_DYN_LDS 0
-#endif
 void launch_prefill_mfma(const void* q, int64_t q_stride, const void* k_cache, const void* v_cache,
                          const int32_t* cu_q, const int32_t* cu_k, const int32_t* block_table, int32_t mbps,
                          int32_t batch, int32_t max_seqlen_q, int32_t Hq, int32_t Hkv, int32_t block_size,
@@ -196,7 +193,7 @@ void launch_prefill_mfma(const void* q, int64_t q_stride, const void* k_cache, c
   const uint16_t* kc = static_cast<const uint16_t*>(k_cache);
   const uint16_t* vc = static_cast<const uint16_t*>(v_cache);
 #define PA_LAUNCH_PF(A, P)                                                                                      \
-  hipLaunchKernelGGL((prefill_mfma_kernel<A, P>), dim3(grid), dim3(kPreThreads), PA_PF_DYN_LDS, stream, qp, q_stride, kc, vc, \
+  hipLaunchKernelGGL((prefill_mfma_kernel<A, P>), dim3(grid), dim3(kPreThreads), 0, stream, qp, q_stride, kc, vc, \
                      cu_q, cu_k, block_table, mbps, batch, Hq, Hkv, block_size, shift, sl2, out, int(out_bf16),  \
                      n_qtiles, n_work)
   if (aligned && pow2) PA_LAUNCH_PF(true, true);
