@@ -81,3 +81,63 @@ def test_graph_store_decode_replays(batch, split):
         assert torch.isfinite(out_e).all(), f"replay {r}: eager output not finite"
         assert torch.equal(out_g, out_e), f"replay {r}: graph output differs from the eager calls"
         assert torch.equal(kc_g, kc_e) and torch.equal(vc_g, vc_e), f"replay {r}: caches differ"
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("batch", [1, 8, 64])
+def test_graph_fused_metadata_store_decode_replays(batch):
+    """The decode step as the engine runs it, metadata and store in one launch (pa_build_metadata_store) and then
+    the balanced decode, captured once and replayed with new cached lengths, queries and K/V."""
+    rng = np.random.default_rng(950 + batch)
+    mbps = 8
+    nb = batch * mbps + 4
+    perm = rng.permutation(nb).astype(np.int32)
+    table = perm[: batch * mbps].reshape(batch, mbps)
+    pool_k = _bf16(rng, (nb, BS, HKV, D))
+    pool_v = _bf16(rng, (nb, BS, HKV, D))
+    kc_g, vc_g = pool_k.to(DEV), pool_v.to(DEV)
+    kc_e, vc_e = kc_g.clone(), vc_g.clone()
+
+    q = torch.empty((batch, HQ, D), dtype=torch.bfloat16, device=DEV)
+    k_new = torch.empty((batch, HKV, D), dtype=torch.bfloat16, device=DEV)
+    v_new = torch.empty_like(k_new)
+    num_cached = torch.empty(batch, dtype=torch.int32, device=DEV)
+    num_new = torch.ones(batch, dtype=torch.int32, device=DEV)
+    bt = torch.from_numpy(table).to(DEV)
+    out_g = torch.empty((batch, HQ, D), dtype=torch.float32, device=DEV)
+    out_e = torch.empty_like(out_g)
+    need = pa.decode_workspace_bytes(batch, HQ, HKV, D, mbps, BS, 0)
+    ws_g = torch.empty(max(need, 16), dtype=torch.uint8, device=DEV)
+    ws_e = torch.empty_like(ws_g)
+    scale = 1.0 / np.sqrt(D)
+
+    def draw():
+        cached = rng.integers(0, mbps * BS, size=batch).astype(np.int32)   # the new token fits the table
+        q.copy_(_bf16(rng, (batch, HQ, D)).to(DEV))
+        k_new.copy_(_bf16(rng, (batch, HKV, D)).to(DEV))
+        v_new.copy_(_bf16(rng, (batch, HKV, D)).to(DEV))
+        num_cached.copy_(torch.from_numpy(cached).to(DEV))
+        torch.cuda.synchronize()
+
+    def step(kc, vc, out, ws):
+        meta = pa.build_metadata_store(num_cached, num_new, bt, batch, k_new, v_new, kc, vc)
+        pa.decode(q, kc, vc, meta["context_lens"], bt, scale, out=out, workspace=ws)
+        return meta
+
+    draw()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        meta_g = step(kc_g, vc_g, out_g, ws_g)
+    torch.cuda.synchronize()
+    for r in range(4):
+        if r > 0:
+            draw()
+        g.replay()
+        torch.cuda.synchronize()
+        meta_e = step(kc_e, vc_e, out_e, ws_e)
+        torch.cuda.synchronize()
+        assert torch.isfinite(out_e).all(), f"replay {r}: eager output not finite"
+        for key in ("slot_mapping", "context_lens", "positions", "cu_seqlens_k"):
+            assert torch.equal(meta_g[key], meta_e[key]), f"replay {r}: {key} differs"
+        assert torch.equal(out_g, out_e), f"replay {r}: graph output differs from the eager calls"
+        assert torch.equal(kc_g, kc_e) and torch.equal(vc_g, vc_e), f"replay {r}: caches differ"
