@@ -73,7 +73,8 @@ int pa_version(void);
  *   cu_seqlens_k [batch+1]  prefix sums of k_len
  *   context_lens [batch]    k_len
  *   positions    [total_q]  absolute position of each flattened new token
- *   slot_mapping [total_q]  block_table[s][pos / block_size] * block_size + pos % block_size
+ *   slot_mapping [total_q]  block_table[s][pos / block_size] * block_size + pos % block_size, or -1 when pos
+ *                           is negative or beyond the row (pos / block_size >= max_blocks_per_seq)
  * This is the flattening of the prepare_prefill example ("一个 prompt 的一生" §3.3.2: positions, cu_seqlens_q and
  * slot_mapping for two sequences with block_size 4) and the slot formula ("Nano-vLLM 架构详解" §1, Step2). For
  * a decode step pass num_new = 1 for every sequence.
@@ -121,6 +122,43 @@ pa_status pa_build_metadata_store(const int32_t* num_cached, const int32_t* num_
                                   int64_t k_tok_stride, const void* v, int64_t v_tok_stride, void* k_cache,
                                   void* v_cache, int32_t num_kv_heads, int32_t head_dim, pa_dtype dtype,
                                   void* stream);
+
+/*
+ * pa_check_indices -- validate the index arrays of a call before making it (a debugging aid).
+ *
+ * The path trusts the indices it is given: an out-of-range slot or block id, or a length beyond the table, is
+ * undefined behaviour there. This call reads only the index arrays (never the caches) and counts, per kind,
+ * the entries that would make the path go out of bounds or compute the wrong rows:
+ *   PA_CHECK_SLOT   slot_mapping[t] >= num_blocks * block_size (negative slots mean "skip" and are valid)
+ *   PA_CHECK_TABLE  a used block-table entry (entries 0 .. ceil(k_len / block_size) - 1 of a sequence) outside
+ *                   [0, num_blocks)
+ *   PA_CHECK_LEN    a key length k_len < 0 or > max_blocks_per_seq * block_size (its table row is then not read)
+ *   PA_CHECK_CU     cu_seqlens_q / cu_seqlens_k not starting at 0 or decreasing, or cu_seqlens_q[batch] !=
+ *                   num_tokens
+ *   PA_CHECK_Q_GT_K q_len > k_len for a sequence (prefill)
+ * The key lengths come from context_lens (decode) or from cu_seqlens_k (prefill); give at most one of them.
+ * Every array may be NULL to skip its checks (block_table is needed when key lengths are given).
+ *   slot_mapping  (device) [num_tokens] or NULL
+ *   block_table   (device) [batch, max_blocks_per_seq]
+ *   context_lens  (device) [batch] or NULL; cu_seqlens_q, cu_seqlens_k (device) [batch + 1] or NULL
+ *   report        (device) uint32 [2 * PA_CHECK_KINDS], written by the call: report[k] is the number of errors
+ *                 of kind k, report[PA_CHECK_KINDS + k] the smallest offending index (token t, sequence s,
+ *                 prefix index i, or s * max_blocks_per_seq + block for PA_CHECK_TABLE), 0xffffffff if none.
+ * Asynchronous like every other call: read the report after the stream has passed it.
+ */
+typedef enum {
+  PA_CHECK_SLOT = 0,
+  PA_CHECK_TABLE = 1,
+  PA_CHECK_LEN = 2,
+  PA_CHECK_CU = 3,
+  PA_CHECK_Q_GT_K = 4,
+  PA_CHECK_KINDS = 5
+} pa_check_kind;
+
+pa_status pa_check_indices(const int32_t* slot_mapping, int32_t num_tokens, const int32_t* block_table,
+                           int32_t batch, int32_t max_blocks_per_seq, const int32_t* context_lens,
+                           const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int32_t num_blocks,
+                           int32_t block_size, uint32_t* report, void* stream);
 
 /*
  * pa_norm_rope_store_kvcache -- the layer's pre-attention step for the new tokens in one pass: k_norm, rotary

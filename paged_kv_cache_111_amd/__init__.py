@@ -6,9 +6,13 @@ The Python functions below only marshal torch tensors into the C calls; see bind
 """
 
 from .binding import (  # noqa: F401
+    CHECK_KINDS,
     PAError,
+    PAIndexError,
     build_metadata,
     build_metadata_store,
+    check_indices,
+    checked_mode,
     decode,
     decode_split_tokens,
     decode_workspace_bytes,
@@ -23,7 +27,7 @@ from .binding import (  # noqa: F401
 )
 
 __all__ = [
-    "PAError", "build_metadata", "build_metadata_store", "decode", "decode_split_tokens", "decode_workspace_bytes",
-    "lib", "norm_rope_store_kvcache", "sample", "sample_workspace_bytes",
-    "prefill_varlen", "prefill_workspace_bytes", "status_str", "store_kvcache",
+    "CHECK_KINDS", "PAError", "PAIndexError", "build_metadata", "build_metadata_store", "check_indices",
+    "checked_mode", "decode", "decode_split_tokens", "decode_workspace_bytes", "lib", "norm_rope_store_kvcache",
+    "prefill_varlen", "prefill_workspace_bytes", "sample", "sample_workspace_bytes", "status_str", "store_kvcache",
 ]

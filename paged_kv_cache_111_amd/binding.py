@@ -36,6 +36,8 @@ SIGNATURES = {
     "pa_build_metadata_store": (ctypes.c_int, [_c_ptr, _c_ptr, _c_ptr, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32,
                                                _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_i64, _c_ptr,
                                                _c_i64, _c_ptr, _c_ptr, _c_i32, _c_i32, ctypes.c_int, _c_ptr]),
+    "pa_check_indices": (ctypes.c_int, [_c_ptr, _c_i32, _c_ptr, _c_i32, _c_i32, _c_ptr, _c_ptr, _c_ptr, _c_i32,
+                                        _c_i32, _c_ptr, _c_ptr]),
     "pa_norm_rope_store_kvcache": (ctypes.c_int, [_c_ptr, _c_i64, _c_ptr, _c_i64, _c_ptr, _c_ptr, _c_i64, _c_ptr,
                                                   _c_ptr, _c_i32, _c_f32, _c_ptr, _c_ptr, _c_i32, _c_ptr, _c_ptr,
                                                   _c_ptr, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, ctypes.c_int,
@@ -61,6 +63,25 @@ class PAError(RuntimeError):
     def __init__(self, fn: str, status: int):
         self.status = status
         super().__init__(f"{fn} failed: {status_str(status)}")
+
+
+# pa_check_kind, in order
+CHECK_KINDS = ("slot", "table", "len", "cu", "q_gt_k")
+
+
+class PAIndexError(ValueError):
+    """Index arrays that the path would follow out of bounds (raised in checked mode, before the launch)."""
+
+    def __init__(self, fn: str, report: dict):
+        self.report = report
+        detail = ", ".join(f"{k}: {v['count']} (first at {v['first']})" for k, v in report.items())
+        super().__init__(f"{fn}: invalid indices: {detail}")
+
+
+def checked_mode() -> bool:
+    """True when PA_CHECKED is set (and not 0): every call then validates its index arrays with
+    pa_check_indices first, synchronising, and raises PAIndexError instead of launching on bad ones."""
+    return os.environ.get("PA_CHECKED", "0") not in ("", "0")
 
 
 def lib() -> ctypes.CDLL:
@@ -149,7 +170,46 @@ def build_metadata(num_cached, num_new, block_table, total_q: int, num_blocks: i
                                  _ptr(out["cu_seqlens_k"]), _ptr(out["context_lens"]), _ptr(out["positions"]),
                                  _ptr(out["slot_mapping"]), _stream(stream))
     _check("pa_build_metadata", st)
+    if checked_mode() and B > 0:
+        _validate("pa_build_metadata", num_blocks=num_blocks, block_size=block_size,
+                  slot_mapping=out["slot_mapping"], block_table=block_table, context_lens=out["context_lens"],
+                  stream=stream)
     return out
+
+
+def check_indices(num_blocks: int, block_size: int, slot_mapping=None, num_tokens=None, block_table=None,
+                  context_lens=None, cu_seqlens_q=None, cu_seqlens_k=None, stream=None) -> dict:
+    """pa_check_indices on the given arrays (None skips their checks). Synchronises and returns
+    {kind: {"count": n, "first": smallest offending index or None}} for the kinds in CHECK_KINDS."""
+    for t, n in ((slot_mapping, "slot_mapping"), (block_table, "block_table"), (context_lens, "context_lens"),
+                 (cu_seqlens_q, "cu_seqlens_q"), (cu_seqlens_k, "cu_seqlens_k")):
+        if t is not None:
+            _i32(t, n)
+    if num_tokens is None:
+        num_tokens = int(slot_mapping.shape[0]) if slot_mapping is not None else 0
+    if block_table is not None:
+        batch, mbps = int(block_table.shape[0]), int(block_table.shape[1])
+    else:
+        batch = int(cu_seqlens_q.shape[0]) - 1 if cu_seqlens_q is not None else 0
+        mbps = 0
+    dev = next(t.device for t in (slot_mapping, block_table, context_lens, cu_seqlens_q, cu_seqlens_k)
+               if t is not None)
+    report = torch.empty(2 * len(CHECK_KINDS), dtype=torch.int32, device=dev)
+    st = lib().pa_check_indices(_ptr(slot_mapping), int(num_tokens), _ptr(block_table), batch, mbps,
+                                _ptr(context_lens), _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), int(num_blocks),
+                                int(block_size), _ptr(report), _stream(stream))
+    _check("pa_check_indices", st)
+    torch.cuda.synchronize(dev)
+    r = report.cpu().numpy().view("uint32")
+    n = len(CHECK_KINDS)
+    return {k: {"count": int(r[i]), "first": None if r[n + i] == 0xFFFFFFFF else int(r[n + i])}
+            for i, k in enumerate(CHECK_KINDS)}
+
+
+def _validate(fn: str, **kw) -> None:
+    bad = {k: v for k, v in check_indices(**kw).items() if v["count"]}
+    if bad:
+        raise PAIndexError(fn, bad)
 
 
 def store_kvcache(k, v, k_cache, v_cache, slot_mapping, stream=None) -> None:
@@ -161,6 +221,8 @@ def store_kvcache(k, v, k_cache, v_cache, slot_mapping, stream=None) -> None:
     _i32(slot_mapping, "slot_mapping")
     T = int(k.shape[0])
     _require(v.shape[0] == T and slot_mapping.shape[0] == T, "k, v and slot_mapping must have one row per token")
+    if checked_mode() and T > 0:
+        _validate("pa_store_kvcache", num_blocks=nb, block_size=bs, slot_mapping=slot_mapping, stream=stream)
     st = lib().pa_store_kvcache(_ptr(k), ks, _ptr(v), vs, _ptr(k_cache), _ptr(v_cache), _ptr(slot_mapping), T, hkv,
                                 d, nb, bs, _dtype_code(k_cache.dtype), _stream(stream))
     _check("pa_store_kvcache", st)
@@ -177,6 +239,10 @@ def build_metadata_store(num_cached, num_new, block_table, total_q: int, k, v, k
     ks = _token_rows(k, hkv, d, "k")
     vs = _token_rows(v, hkv, d, "v")
     _require(k.shape[0] == total_q and v.shape[0] == total_q, "k and v must have one row per new token")
+    if checked_mode():
+        meta = build_metadata(num_cached, num_new, block_table, total_q, nb, bs, stream=stream)
+        store_kvcache(k, v, k_cache, v_cache, meta["slot_mapping"], stream=stream)
+        return meta
     B = int(num_new.shape[0])
     dev = num_new.device
     out = {
@@ -221,6 +287,9 @@ def norm_rope_store_kvcache(k, v, k_cache, v_cache, slot_mapping, k_norm_weight,
         if q_out is None:
             q_out = torch.empty((T, hq, d), dtype=q.dtype, device=q.device)
         _require(q_out.is_contiguous() and tuple(q_out.shape) == (T, hq, d), "q_out must be contiguous [T, Hq, D]")
+    if checked_mode() and T > 0:
+        _validate("pa_norm_rope_store_kvcache", num_blocks=nb, block_size=bs, slot_mapping=slot_mapping,
+                  stream=stream)
     st = lib().pa_norm_rope_store_kvcache(_ptr(k), ks, _ptr(v), vs, _ptr(k_norm_weight), _ptr(q), qs,
                                           _ptr(q_norm_weight), _ptr(q_out), hq, float(rms_eps), _ptr(positions),
                                           _ptr(cos_sin), int(cos_sin.shape[0]), _ptr(k_cache), _ptr(v_cache),
@@ -273,6 +342,9 @@ def prefill_varlen(q, k_cache, v_cache, cu_seqlens_q, cu_seqlens_k, block_table,
     if out is None:
         out = torch.empty((T, hq, d), dtype=out_dtype, device=q.device)
     _require(out.is_contiguous() and tuple(out.shape) == (T, hq, d), "out must be contiguous [total_q, Hq, D]")
+    if checked_mode() and B > 0:
+        _validate("pa_prefill_varlen", num_blocks=nb, block_size=bs, num_tokens=T, block_table=block_table,
+                  cu_seqlens_q=cu_seqlens_q, cu_seqlens_k=cu_seqlens_k, stream=stream)
     need = prefill_workspace_bytes(B, hq, d, max_seqlen_q, max_seqlen_k)
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
@@ -311,6 +383,9 @@ def decode(q, k_cache, v_cache, context_lens, block_table, softmax_scale: float,
     if out is None:
         out = torch.empty((B, hq, d), dtype=out_dtype, device=q.device)
     _require(out.is_contiguous() and tuple(out.shape) == (B, hq, d), "out must be contiguous [B, Hq, D]")
+    if checked_mode() and B > 0:
+        _validate("pa_decode", num_blocks=nb, block_size=bs, block_table=block_table, context_lens=context_lens,
+                  stream=stream)
     need = decode_workspace_bytes(B, hq, hkv, d, mbps, bs, split_tokens)
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)

@@ -15,7 +15,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libpa.so")
 SOURCES = ["pa_api.hip", "pa_meta_store.hip", "pa_generic.hip", "pa_decode.hip", "pa_decode_stream.hip",
-           "pa_prefill.hip", "pa_rope_store.hip", "pa_sample.hip"]
+           "pa_prefill.hip", "pa_rope_store.hip", "pa_sample.hip", "pa_check.hip"]
 ARCH = "gfx950"
 
 # Packed fp32 VALU instructions are kept out of every kernel (plain float code only).

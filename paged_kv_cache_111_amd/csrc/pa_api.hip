@@ -156,6 +156,25 @@ pa_status pa_build_metadata_store(const int32_t* num_cached, const int32_t* num_
   return launched();
 }
 
+pa_status pa_check_indices(const int32_t* slot_mapping, int32_t num_tokens, const int32_t* block_table,
+                           int32_t batch, int32_t max_blocks_per_seq, const int32_t* context_lens,
+                           const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int32_t num_blocks,
+                           int32_t block_size, uint32_t* report, void* stream) {
+  if (num_tokens < 0 || batch < 0 || num_blocks <= 0 || block_size <= 0) return PA_ERR_SHAPE;
+  if (int64_t(num_blocks) * block_size > kInt32Max) return PA_ERR_SHAPE;
+  if (context_lens && cu_seqlens_k) return PA_ERR_SHAPE;  // one source of key lengths
+  if (!report || !aligned(report, 4)) return PA_ERR_NULL;
+  if (num_tokens > 0 && !slot_mapping && !cu_seqlens_q) return PA_ERR_NULL;
+  if (batch > 0 && (context_lens || cu_seqlens_k)) {
+    if (!block_table) return PA_ERR_NULL;
+    if (max_blocks_per_seq <= 0) return PA_ERR_SHAPE;
+  }
+  pa::launch_check_indices(num_tokens > 0 ? slot_mapping : nullptr, num_tokens, block_table, batch,
+                           max_blocks_per_seq, context_lens, cu_seqlens_q, cu_seqlens_k, num_blocks, block_size,
+                           report, static_cast<hipStream_t>(stream));
+  return launched();
+}
+
 pa_status pa_norm_rope_store_kvcache(const void* k, int64_t k_tok_stride, const void* v, int64_t v_tok_stride,
                                      const void* k_norm_weight, const void* q, int64_t q_tok_stride,
                                      const void* q_norm_weight, void* q_out, int32_t num_heads, float rms_eps,

@@ -15,6 +15,11 @@ void launch_metadata_store(const int32_t* num_cached, const int32_t* num_new, co
                            int64_t k_stride_bytes, const void* v, int64_t v_stride_bytes, void* k_cache,
                            void* v_cache, int64_t row_bytes, int vec_bytes, hipStream_t stream);
 
+void launch_check_indices(const int32_t* slot_mapping, int32_t num_tokens, const int32_t* block_table,
+                          int32_t batch, int32_t mbps, const int32_t* context_lens, const int32_t* cu_q,
+                          const int32_t* cu_k, int32_t num_blocks, int32_t block_size, uint32_t* report,
+                          hipStream_t stream);
+
 void launch_store_kvcache(const void* k, int64_t k_stride_bytes, const void* v, int64_t v_stride_bytes,
                           void* k_cache, void* v_cache, const int32_t* slot_mapping, int32_t num_tokens,
                           int64_t row_bytes, int vec_bytes, hipStream_t stream);

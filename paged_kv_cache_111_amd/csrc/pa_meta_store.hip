@@ -79,7 +79,8 @@ __device__ __forceinline__ void meta_prefix_sums(const int32_t* __restrict__ num
 }
 
 // Sequence of new token t (the largest s with cu_q[s] <= t: sequences with no new tokens have
-// cu_q[s] == cu_q[s + 1] and are skipped), its absolute position and its slot.
+// cu_q[s] == cu_q[s + 1] and are skipped), its absolute position and its slot (-1 for a position outside the
+// sequence's row of the block table).
 __device__ __forceinline__ int32_t meta_token(int32_t t, const int32_t* cu_q, int32_t batch,
                                               const int32_t* __restrict__ num_cached,
                                               const int32_t* __restrict__ block_table, int32_t mbps,
@@ -91,6 +92,7 @@ __device__ __forceinline__ int32_t meta_token(int32_t t, const int32_t* cu_q, in
   }
   pos = num_cached[a] + (t - cu_q[a]);
   const int32_t blk = pos / block_size;
+  if (pos < 0 || blk >= mbps) return -1;  // outside the sequence's table row: no slot (and no read past the row)
   return block_table[int64_t(a) * mbps + blk] * block_size + (pos - blk * block_size);
 }
 

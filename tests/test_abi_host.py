@@ -90,6 +90,31 @@ def test_metadata_store_rejects_bad_arguments():
     assert _meta_store(**dev, k=fake + 1, v=fake, kc=fake, vc=fake) == b.PA_ERR_SHAPE  # misaligned bf16 row
 
 
+def test_check_indices_rejects_bad_arguments():
+    lib = pa.lib()
+    fake = 0x10000  # never dereferenced: every call below returns before a launch
+    rep = fake
+    #                         slots  T  table batch mbps ctx   cu_q  cu_k  nb  bs  report
+    assert lib.pa_check_indices(fake, 4, fake, 2, 8, fake, NULL, NULL, 16, 256, NULL, NULL) == b.PA_ERR_NULL
+    assert lib.pa_check_indices(fake, 4, fake, 2, 8, fake, NULL, fake, 16, 256, rep, NULL) == b.PA_ERR_SHAPE
+    assert lib.pa_check_indices(fake, 4, NULL, 2, 8, fake, NULL, NULL, 16, 256, rep, NULL) == b.PA_ERR_NULL
+    assert lib.pa_check_indices(fake, 4, fake, 2, 0, fake, NULL, NULL, 16, 256, rep, NULL) == b.PA_ERR_SHAPE
+    assert lib.pa_check_indices(fake, -1, fake, 2, 8, fake, NULL, NULL, 16, 256, rep, NULL) == b.PA_ERR_SHAPE
+    assert lib.pa_check_indices(fake, 4, fake, 2, 8, fake, NULL, NULL, 0, 256, rep, NULL) == b.PA_ERR_SHAPE
+    assert lib.pa_check_indices(NULL, 4, fake, 2, 8, fake, NULL, NULL, 16, 256, rep, NULL) == b.PA_ERR_NULL
+    assert lib.pa_check_indices(fake, 4, fake, 2, 8, fake, NULL, NULL, 2 ** 24, 256, rep, NULL) == b.PA_ERR_SHAPE
+    assert lib.pa_check_indices(fake, 4, fake, 2, 8, fake, NULL, NULL, 16, 256, rep + 2, NULL) == b.PA_ERR_NULL
+
+
+def test_checked_mode_follows_the_environment(monkeypatch):
+    monkeypatch.delenv("PA_CHECKED", raising=False)
+    assert not pa.checked_mode()
+    monkeypatch.setenv("PA_CHECKED", "0")
+    assert not pa.checked_mode()
+    monkeypatch.setenv("PA_CHECKED", "1")
+    assert pa.checked_mode()
+
+
 def _prefill(**kw):
     args = dict(q=NULL, qs=32 * 128, kc=NULL, vc=NULL, cq=NULL, ck=NULL, bt=NULL, mbps=8, batch=2, total_q=10,
                 msq=8, msk=8, hq=32, hkv=8, d=128, nb=16, bs=256, scale=0.1, dtype=1, out=NULL, odt=0, ws=NULL,
