@@ -127,15 +127,12 @@ __device__ __forceinline__ float pf_halfmax(const f32x16 (&sc)[kSub]) {
 }
 
 // Weights of one tile (fp16, round to nearest; the row sum is taken over the rounded weights that enter the PV
-// product, so the weights the output averages with sum to one) and O^T += V^T P^T from the V tile in LDS.
+// product, so the weights the output averages with sum to one), as the B operand of the PV MFMA.
 // Lane group g4 = lane / 16 (half hh = g4 / 2, d offset 16 (g4 % 2)); for k-step kk the lane's slots 0..3 are
 // keys 16 kk + 4 hh + 0..3 and slots 4..7 keys 16 kk + 8 + 4 hh + 0..3.
-// All weights are formed first and the 16 MFMAs then run back to back: vector instructions placed between one
-// wave's MFMAs stall its issue, while the other wave on the SIMD can run its vector work during them.
-__device__ __forceinline__ void pf_weights_pv(const f32x16 (&sc)[kSub], f32x16 (&o)[4], float m, float& lsum,
-                                              const uint16_t* vt, int va_off, float scale_log2) {
+__device__ __forceinline__ void pf_weights(const f32x16 (&sc)[kSub], f16x8 (&pb)[kSub][2], float m, float& lsum,
+                                           float scale_log2) {
   float psum[2] = {0.f, 0.f};  // two independent chains
-  f16x8 pb[kSub][2];
 #pragma unroll
   for (int sub = 0; sub < kSub; ++sub) {
 #pragma unroll
@@ -149,6 +146,11 @@ __device__ __forceinline__ void pf_weights_pv(const f32x16 (&sc)[kSub], f32x16 (
       pb[sub][kk] = as_f16x8(pw);
     }
   }
+  lsum += psum[0] + psum[1];
+}
+
+// O^T += V^T P^T from the V tile in LDS: 16 MFMAs back to back.
+__device__ __forceinline__ void pf_pv(const f16x8 (&pb)[kSub][2], f32x16 (&o)[4], const uint16_t* vt, int va_off) {
 #pragma unroll
   for (int sub = 0; sub < kSub; ++sub) {
 #pragma unroll
@@ -163,7 +165,16 @@ __device__ __forceinline__ void pf_weights_pv(const f32x16 (&sc)[kSub], f32x16 (
       }
     }
   }
-  lsum += psum[0] + psum[1];
+}
+
+// The tile's weights, then its PV product. All weights are formed before the 16 MFMAs run: vector instructions
+// placed between one wave's MFMAs stall its issue, while the other wave on the SIMD can run its vector work
+// during them.
+__device__ __forceinline__ void pf_weights_pv(const f32x16 (&sc)[kSub], f32x16 (&o)[4], float m, float& lsum,
+                                              const uint16_t* vt, int va_off, float scale_log2) {
+  f16x8 pb[kSub][2];
+  pf_weights(sc, pb, m, lsum, scale_log2);
+  pf_pv(pb, o, vt, va_off);
 }
 
 }  // namespace pa
