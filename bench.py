@@ -161,6 +161,70 @@ def write_traffic_summary(workload: str, fetch_csv: str, write_csv: str) -> dict
     return out
 
 
+SQ_PASSES = {
+    "A": "SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CYCLES SQ_INSTS_VALU SQ_INSTS_MFMA SQ_ACTIVE_INST_VALU SQ_WAVE_CYCLES "
+         "SQ_INSTS_VALU_TRANS_F32 GRBM_GUI_ACTIVE",
+    "B": "SQ_LDS_BANK_CONFLICT SQ_LDS_IDX_ACTIVE SQ_VALU_MFMA_COEXEC_CYCLES SQ_INSTS_LDS SQ_WAIT_INST_LDS "
+         "SQ_WAIT_INST_ANY SQ_WAVE_CYCLES GRBM_GUI_ACTIVE",
+}
+N_SIMDS = 256 * 4
+
+
+def write_sq_summary(workload: str, csv_a: str, csv_b: str) -> dict:
+    """profiles/<workload>_sq_counters.json from two rocprofv3 --pmc runs of this script (the counter sets of
+    SQ_PASSES, eight counters per run at most): the attention kernel's mean counters per dispatch and the
+    fractions they give. GRBM_GUI_ACTIVE is summed over the 8 XCDs, so the kernel's cycles are an eighth of it; MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (cycles x 1024 SIMDs)."""
+    import collections
+    import csv
+
+    from workloads import make_config
+
+    kind = make_config(workload, fill=False).steps[-1].kind
+    kern = ATTN_KERNELS[kind][0]
+    vals = {}
+    for path in (csv_a, csv_b):
+        agg = collections.defaultdict(list)
+        with open(path, newline="") as f:
+            for r in csv.DictReader(f):
+                if kern in r["Kernel_Name"]:
+                    agg[r["Counter_Name"]].append(float(r["Counter_Value"]))
+        if not agg:
+            raise SystemExit(f"no dispatch of {kern} in {path}")
+        for k, v in agg.items():
+            vals.setdefault(k, sum(v) / len(v))
+    cycles = vals["GRBM_GUI_ACTIVE"] / 8
+    frac = {
+        "mfma_busy": vals["SQ_VALU_MFMA_BUSY_CYCLES"] / (cycles * N_SIMDS),
+        "mfma_valu_coexec_per_mfma_busy": vals["SQ_VALU_MFMA_COEXEC_CYCLES"] / vals["SQ_VALU_MFMA_BUSY_CYCLES"],
+        "valu_insts_per_mfma": vals["SQ_INSTS_VALU"] / vals["SQ_INSTS_MFMA"],
+        "trans_f32_per_mfma": vals["SQ_INSTS_VALU_TRANS_F32"] / vals["SQ_INSTS_MFMA"],
+        "valu_active_per_wave_cycle": vals["SQ_ACTIVE_INST_VALU"] / vals["SQ_WAVE_CYCLES"],
+        "lds_wait_per_wave_cycle": vals["SQ_WAIT_INST_LDS"] / vals["SQ_WAVE_CYCLES"],
+        "any_wait_per_wave_cycle": vals["SQ_WAIT_INST_ANY"] / vals["SQ_WAVE_CYCLES"],
+        "lds_bank_conflict_per_lds_active": vals["SQ_LDS_BANK_CONFLICT"] / max(1.0, vals["SQ_LDS_IDX_ACTIVE"]),
+    }
+    out = {
+        "workload": workload,
+        "kernel": kern,
+        "what": "SQ counters of the attention kernel, mean per dispatch (totals over the GPU), and fractions: MFMA "
+                "busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 XCDs x 1024 SIMDs)",
+        "commands": [f"cd /tmp && rocprofv3 --pmc {SQ_PASSES[p]} -d gpurun_out/sq{p}_{workload} -o pmc "
+                     f"--output-format csv -- python /root/repo/bench.py --only {workload} --no-cpu-baseline "
+                     f"--steps 5 --warmup 2 --prewarm 0" for p in ("A", "B")]
+                    + [f"python bench.py --only {workload} --sq-summary gpurun_out/sqA_{workload}/"
+                       f"pmc_counter_collection.csv gpurun_out/sqB_{workload}/pmc_counter_collection.csv"],
+        "counters": {k: round(v, 1) for k, v in sorted(vals.items())},
+        "kernel_cycles": round(cycles, 1),
+        "fractions": {k: round(v, 4) for k, v in frac.items()},
+        "source_files": list(ATTN_SOURCES[kind]),
+        "source_sha": _src_sha(*ATTN_SOURCES[kind]),
+    }
+    with open(os.path.join(ROOT, "profiles", f"{workload}_sq_counters.json"), "w", encoding="utf-8") as f:
+        json.dump(out, f, indent=1)
+        f.write("\n")
+    return out
+
+
 class GpuWorkload:
     """A workload's inputs on the device, with n_layers independent cache pools holding the same contents."""
 
@@ -545,6 +609,9 @@ def main() -> int:
     ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"), default=None,
                     help="write the HBM traffic summary of --only's workload from two rocprofv3 counter files "
                          "(no GPU needed) and exit")
+    ap.add_argument("--sq-summary", nargs=2, metavar=("PASS_A_CSV", "PASS_B_CSV"), default=None,
+                    help="write the SQ counter summary of --only's workload from two rocprofv3 counter files "
+                         "(no GPU needed) and exit")
     ap.add_argument("--store-sweep", action="store_true",
                     help="only time store_kvcache at the 0.6B cache shape for 64 .. 131072 tokens")
     ap.add_argument("--sample-sweep", action="store_true",
@@ -564,6 +631,11 @@ def main() -> int:
         if not args.only:
             ap.error("--traffic-summary needs --only WORKLOAD")
         print(json.dumps(write_traffic_summary(args.only, *args.traffic_summary), indent=1))
+        return 0
+    if args.sq_summary:
+        if not args.only:
+            ap.error("--sq-summary needs --only WORKLOAD")
+        print(json.dumps(write_sq_summary(args.only, *args.sq_summary), indent=1))
         return 0
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the attention step runs "
