@@ -95,6 +95,7 @@ __global__ __launch_bounds__(kPreThreads) __attribute__((amdgpu_waves_per_eu(2, 
 #pragma unroll
     for (int i = 0; i < 16; ++i) o[mt][i] = 0.f;
   float m = -INFINITY;  // running reference max of this row, in scaled log2 units
+  bool started = false;  // the wave has set its reference max (wave-uniform)
   float lsum = 0.f;     // this lane's part of the row sum (the two halves are added at the end)
 
   const int li = lane & 15;
@@ -134,11 +135,14 @@ __global__ __launch_bounds__(kPreThreads) __attribute__((amdgpu_waves_per_eu(2, 
       // m + slack means no row above it), and only a tile that moves the reference max exchanges the halves.
       if (__any(mh > m + kRescaleSlack)) {
         const float mn = fmaxf(m, xhalf_max(mh));
-        const float alpha = __builtin_amdgcn_exp2f(m - mn);  // 0 on the first tile (m = -inf)
-        m = mn;
-        lsum *= alpha;
+        if (started) {  // on the wave's first tile O and l are still zero
+          const float alpha = __builtin_amdgcn_exp2f(m - mn);
+          lsum *= alpha;
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt) o[mt] *= alpha;
+          for (int mt = 0; mt < 4; ++mt) o[mt] *= alpha;
+        }
+        m = mn;
+        started = true;
       }
       pf_weights_pv(cur, o, m, lsum, vt[P], va_off, scale_log2);
       pf_lstore_k(kst, kt[P], tid);      // K tile j+2 replaces K tile j (scored in the previous step)
