@@ -51,3 +51,16 @@ def test_prefill_flops_count_visible_pairs(name):
     assert work["flops"] == 4 * wl.head_dim * wl.num_heads * pairs
     if name == "chunked_qwen3_8b":
         assert pairs == 2048 * 30720 + 2048 * 2049 // 2 == 65_012_736
+
+
+def test_bench_refuses_more_than_one_gpu():
+    import os
+    import subprocess
+    import sys
+
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+    assert r.stdout == ""
