@@ -1,8 +1,10 @@
 """Benchmark of the paged-KV attention step on one MI355X.
 
-One step = one pass of the whole path over one batch: device-side metadata (slots, prefix sums) and store_kvcache
-of the new tokens in one launch (two with --separate-store), then attention over the paged cache (decode:
-balanced pass + merge of cut sequences; prefill: one pass).
+One step = one pass of the whole path over one batch. Prefill: device-side metadata (slots, prefix sums) and
+store_kvcache of the new tokens in one launch (two with --separate-store), then attention over the paged cache in
+one pass. Decode: pa_decode_append, whose balanced pass computes each new token's slot from the block table,
+stores its K/V rows and attends over the cache, then merges cut sequences (two launches); with --no-append, the
+metadata + store launch and pa_decode as for prefill.
 
 Main line: the decode workload with Qwen3-0.6B attention shape (64 sequences, 16 query / 8 KV heads, head_dim
 128, bf16, block_size 256, contexts U[128, 4096]). Consecutive steps use different per-layer cache pools (the
@@ -58,11 +60,13 @@ def algorithmic_work(wl, step, out_bytes: int):
     o_bytes = T * wl.num_heads * wl.head_dim * out_bytes
     attn_bytes = kv_bytes + q_bytes + o_bytes + 4 * n_tbl + 4 * B
     store_bytes = 2 * T * kv_tok + 4 * T
+    append_bytes = 2 * T * kv_tok
     meta_bytes = 4 * (3 * B + n_tbl) + 4 * (3 * B + 2 + 2 * T)
     past = k_len - q_len
     pairs = int(np.sum(q_len * past + q_len * (q_len + 1) // 2))
     flops = 4 * wl.head_dim * wl.num_heads * pairs
     return {"kv_bytes": kv_bytes, "attn_bytes": attn_bytes, "store_bytes": store_bytes, "meta_bytes": meta_bytes,
+            "append_bytes": append_bytes,
             "pairs": pairs, "flops": flops, "sum_k": int(k_len.sum()), "tokens": T}
 
 
@@ -228,13 +232,14 @@ def write_sq_summary(workload: str, csv_a: str, csv_b: str) -> dict:
 class GpuWorkload:
     """A workload's inputs on the device, with n_layers independent cache pools holding the same contents."""
 
-    def __init__(self, wl, n_layers: int, out_dtype, fused_store: bool = True):
+    def __init__(self, wl, n_layers: int, out_dtype, fused_store: bool = True, append: bool = True):
         import torch
 
         self.torch = torch
         self.wl = wl
         self.step = wl.steps[-1]
         self.fused_store = fused_store
+        self.append = append and self.step.kind == "decode"
         dev = "cuda:0"
 
         def up(a):
@@ -269,11 +274,21 @@ class GpuWorkload:
 
     def run(self, layer: int, ev=None):
         """One step on layer `layer`'s pool; ev = (e0, e1, e2, e3) events around metadata, store, attention (with
-        the fused launch, e0..e1 spans metadata and store, and e1..e2 is empty)."""
+        the fused launch, e0..e1 spans metadata and store, and e1..e2 is empty; with append, the decode call
+        computes its slots and stores the new rows itself, and e0..e2 is empty)."""
         pa, wl, st = self.pa, self.wl, self.step
         kc, vc = self.k_layers[layer], self.v_layers[layer]
         if ev:
             ev[0].record()
+        if self.append:
+            if ev:
+                ev[1].record()
+                ev[2].record()
+            pa.decode_append(self.q, self.k, self.v, kc, vc, self.num_cached, self.block_table, wl.scale,
+                             out=self.out, workspace=self.ws, fallback=False)
+            if ev:
+                ev[3].record()
+            return
         if self.fused_store:
             meta = pa.build_metadata_store(self.num_cached, self.num_new, self.block_table, self.total_q, self.k,
                                            self.v, kc, vc)
@@ -342,7 +357,8 @@ def time_workload(g: GpuWorkload, steps: int, warmup: int, n_layers: int):
 
 
 def graph_ladder(batches, iters: int = 200):
-    """Host launch overhead of a decode step (store_kvcache + decode) at the Qwen3-0.6B attention shape: wall
+    """Host launch overhead of a decode step (store_kvcache + decode, and pa_decode_append on the same data: the
+    new rows at position length - 1) at the Qwen3-0.6B attention shape: wall
     time per step of eager calls through the binding against one replay of the same calls captured in a HIP
     graph, for a ladder of batch sizes (contexts U{128..4096}, block size 256, one pool, synthetic data). The
     engine captures its decode step per batch size for exactly this overhead ("一个 prompt 的一生：nano-vllm 从起服务到吐出
@@ -375,34 +391,46 @@ def graph_ladder(batches, iters: int = 200):
                          device=dev)
         scale = 1.0 / np.sqrt(D)
 
+        cached = torch.from_numpy((lens - 1).astype(np.int32)).to(dev)
+
         def step():
             pa.store_kvcache(k_new, v_new, kc, vc, sl)
             pa.decode(q, kc, vc, ctx, bt, scale, out=out, workspace=ws)
 
-        for _ in range(10):
-            step()
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for _ in range(iters):
-            step()
-        torch.cuda.synchronize()
-        eager = (time.perf_counter() - t0) / iters
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            step()
-        for _ in range(10):
-            g.replay()
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for _ in range(iters):
-            g.replay()
-        torch.cuda.synchronize()
-        graph = (time.perf_counter() - t0) / iters
+        def step_append():
+            pa.decode_append(q, k_new, v_new, kc, vc, cached, bt, scale, out=out, workspace=ws, fallback=False)
+
+        def eager_and_graph(fn):
+            for _ in range(10):
+                fn()
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(iters):
+                fn()
+            torch.cuda.synchronize()
+            eager = (time.perf_counter() - t0) / iters
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                fn()
+            for _ in range(10):
+                g.replay()
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(iters):
+                g.replay()
+            torch.cuda.synchronize()
+            graph = (time.perf_counter() - t0) / iters
+            del g
+            return eager, graph
+
+        eager, graph = eager_and_graph(step)
+        a_eager, a_graph = eager_and_graph(step_append)
         kv = float(lens.sum()) * 2 * Hkv * D * 2
         rows.append({"batch": B, "eager_us": round(eager * 1e6, 2), "graph_us": round(graph * 1e6, 2),
-                     "kv_GBps_eager": round(kv / eager / 1e9, 1), "kv_GBps_graph": round(kv / graph / 1e9, 1)})
+                     "kv_GBps_eager": round(kv / eager / 1e9, 1), "kv_GBps_graph": round(kv / graph / 1e9, 1),
+                     "append_eager_us": round(a_eager * 1e6, 2), "append_graph_us": round(a_graph * 1e6, 2)})
         print(f"[bench] graph ladder {rows[-1]}", file=sys.stderr, flush=True)
-        del g, kc, vc
+        del kc, vc
         torch.cuda.empty_cache()
     return rows
 
@@ -560,35 +588,49 @@ def cpu_baseline(wl, budget_s: float):
 # ---------------------------------------------------------------------------------------------- main
 
 
-def bench_one(name: str, steps: int, warmup: int, n_layers: int, out_dtype_name: str, fused_store: bool = True):
+def bench_one(name: str, steps: int, warmup: int, n_layers: int, out_dtype_name: str, fused_store: bool = True,
+              append: bool = True):
     import torch
 
     from workloads import make_config
 
     wl = make_config(name)
     out_dtype = torch.bfloat16 if out_dtype_name == "bf16" else torch.float32
-    g = GpuWorkload(wl, n_layers, out_dtype, fused_store)
+    g = GpuWorkload(wl, n_layers, out_dtype, fused_store, append)
     t = time_workload(g, steps, warmup, n_layers)
     work = algorithmic_work(wl, g.step, 2 if out_dtype == torch.bfloat16 else 4)
-    res = {"workload": name, "kind": g.step.kind, "timing": t, "work": work}
+    res = {"workload": name, "kind": g.step.kind, "timing": t, "work": work, "append": g.append}
     if g.step.kind == "decode":
-        res["attn_GBps"] = work["attn_bytes"] / (t["attn_ms"] * 1e-3) / 1e9
+        # with append the decode launch also moves the new rows (read and written); no slot or metadata arrays
+        launch_bytes = work["attn_bytes"] + (work["append_bytes"] if g.append else 0)
+        step_bytes = launch_bytes if g.append else work["attn_bytes"] + work["store_bytes"] + work["meta_bytes"]
+        res["launch_bytes"] = launch_bytes
+        res["attn_GBps"] = launch_bytes / (t["attn_ms"] * 1e-3) / 1e9
         res["attn_frac_hbm"] = res["attn_GBps"] / HBM_PEAK_GBS
-        res["step_GBps"] = (work["attn_bytes"] + work["store_bytes"] + work["meta_bytes"]) / (t["wall_ms_per_step"] * 1e-3) / 1e9
+        res["step_GBps"] = step_bytes / (t["wall_ms_per_step"] * 1e-3) / 1e9
     else:
         res["attn_TFLOPs"] = work["flops"] / (t["attn_ms"] * 1e-3) / 1e12
         res["attn_frac_mfma"] = res["attn_TFLOPs"] / MFMA_BF16_PEAK_TFLOPS
         res["step_TFLOPs"] = work["flops"] / (t["wall_ms_per_step"] * 1e-3) / 1e12
-    if fused_store:
+    if not g.append and fused_store:
         res["meta_store_GBps"] = (work["store_bytes"] + work["meta_bytes"]) / (t["meta_ms"] * 1e-3) / 1e9
-    else:
+    elif not g.append:
         res["store_GBps"] = work["store_bytes"] / (t["store_ms"] * 1e-3) / 1e9
     del g
     torch.cuda.empty_cache()
     return wl, res
 
 
+def _step_text(is_dec: bool, append: bool, fused: bool) -> str:
+    if append:
+        return "decode with the new K/V rows stored in its own pass (balanced pass + merge; slots from the tables)"
+    return (("metadata and store_kvcache in one launch + " if fused else "metadata + store_kvcache + ") +
+            ("decode (balanced pass + merge)" if is_dec else "prefill"))
+
+
 def _store_rate(r) -> dict:
+    if r["append"]:
+        return {"store": "in the decode launch"}
     if "store_GBps" in r:
         return {"store_GBps": round(r["store_GBps"], 1)}
     return {"metadata_store_GBps": round(r["meta_store_GBps"], 1)}
@@ -623,6 +665,9 @@ def main() -> int:
     ap.add_argument("--separate-store", action="store_true",
                     help="metadata and store as two launches (pa_build_metadata, pa_store_kvcache) instead of one "
                          "(pa_build_metadata_store)")
+    ap.add_argument("--no-append", action="store_true",
+                    help="decode: metadata + store launch before pa_decode instead of pa_decode_append (which "
+                         "stores the new rows inside the decode pass)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 1 GiB copy kernel (reference for the HBM byte counters)")
     args = ap.parse_args()
@@ -655,14 +700,15 @@ def main() -> int:
         return 0
     main_name = args.only or "decode_qwen3_0p6b"
     fused = not args.separate_store
-    wl, main = bench_one(main_name, args.steps, args.warmup, args.layers, args.out_dtype, fused)
+    append = not args.no_append
+    wl, main = bench_one(main_name, args.steps, args.warmup, args.layers, args.out_dtype, fused, append)
     print(f"[bench] {main_name}: {json.dumps(main['timing'])}", file=sys.stderr, flush=True)
     secondary = []
     if not args.only and not args.no_secondary:
         for name in ("prefill_qwen3_8b", "chunked_qwen3_8b", "decode_qwen3_32b"):
             layers = 1 if name == "decode_qwen3_32b" else args.layers
             _, r = bench_one(name, max(10, args.steps // 2), max(2, args.warmup // 2), layers, args.out_dtype,
-                             fused)
+                             fused, append)
             print(f"[bench] {name}: {json.dumps(r['timing'])}", file=sys.stderr, flush=True)
             entry = {"workload": name, "attn_ms": round(r["timing"]["attn_ms"], 4),
                      "step_ms": round(r["timing"]["wall_ms_per_step"], 4)}
@@ -691,8 +737,9 @@ def main() -> int:
         value = main["step_GBps"]
         roof = {"bound": "hbm", "achieved": round(main["attn_GBps"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(main["attn_frac_hbm"], 4), "traffic": traffic,
-                "kernel": "pa_decode (" + " + ".join(ATTN_KERNELS["decode"]) + ")",
-                "bytes_per_launch": work["attn_bytes"], "launch_ms": round(t["attn_ms"], 5)}
+                "kernel": ("pa_decode_append (" if main["append"] else "pa_decode (") +
+                          " + ".join(ATTN_KERNELS["decode"]) + ")",
+                "bytes_per_launch": main["launch_bytes"], "launch_ms": round(t["attn_ms"], 5)}
         unit = "GB/s"
     else:
         value = work["flops"] / (t["wall_ms_per_step"] * 1e-3) / 1e12
@@ -711,9 +758,8 @@ def main() -> int:
                    "num_kv_heads": wl.num_kv_heads, "head_dim": wl.head_dim, "block_size": wl.block_size,
                    "sum_context": work["sum_k"], "new_tokens": work["tokens"], "seed": wl.seed,
                    "out_dtype": args.out_dtype, "layers_cycled": args.layers,
-                   "step": ("metadata and store_kvcache in one launch + " if fused else "metadata + store_kvcache + ")
-                   + ("decode (balanced pass + merge)" if is_dec else "prefill")},
-        "breakdown_ms": ({"metadata_store": round(t["meta_ms"], 5)} if fused else
+                   "step": _step_text(is_dec, main["append"], fused)},
+        "breakdown_ms": ({} if main["append"] else {"metadata_store": round(t["meta_ms"], 5)} if fused else
                          {"metadata": round(t["meta_ms"], 5), "store": round(t["store_ms"], 5)}) |
                         {"attention": round(t["attn_ms"], 5), "attention_median": round(t["attn_ms_median"], 5),
                          "events_step": round(t["step_ms"], 5),

@@ -241,6 +241,32 @@ pa_status pa_decode(const void* q, int64_t q_tok_stride, const void* k_cache, co
                     int32_t block_size, float softmax_scale, pa_dtype dtype, void* out, pa_dtype out_dtype,
                     int32_t split_tokens, void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * pa_decode_append -- the decode step with the new token's K and V given: store them, then decode.
+ *
+ * The same as pa_store_kvcache of k_new[s], v_new[s] at position num_cached[s] of sequence s (slot
+ * block_table[s][pos / block_size] * block_size + pos % block_size, pos = num_cached[s]) followed by pa_decode
+ * over context_lens[s] = num_cached[s] + 1 keys, in the balanced decode's two launches instead of four: the
+ * worker whose slice holds a pair's new key writes that head of the new rows and then reads them as part of its
+ * slice. FlashAttention's decode call takes the new k, v the same way and updates the cache in place ("Nano-vLLM
+ * 架构详解" §3.2, flash_attn_with_kvcache; the step is store then attention, "一个 prompt 的一生" §4).
+ *   q      (device) [batch, num_heads, head_dim]; k_new, v_new (device) [batch, num_kv_heads, head_dim], token
+ *          stride *_tok_stride elements (a multiple of 8), 16-byte aligned
+ *   num_cached (device) [batch] int32: keys already in the cache; the table row must hold num_cached[s] + 1
+ *   workspace at least pa_decode_workspace_bytes(batch, ..., split_tokens = 0) bytes
+ * Taken for the shapes the balanced decode takes (bf16, head_dim 128, at most 16 query heads per KV head, block
+ * size a multiple of 32, batch <= 4096, 16-byte aligned pointers); PA_ERR_UNSUPPORTED otherwise, before any
+ * launch (then call pa_build_metadata_store and pa_decode). As in pa_decode the indices are trusted: the row's
+ * entries up to position num_cached[s] must be valid block ids (pa_check_indices with context_lens =
+ * num_cached + 1 checks them).
+ */
+pa_status pa_decode_append(const void* q, int64_t q_tok_stride, const void* k_new, int64_t k_tok_stride,
+                           const void* v_new, int64_t v_tok_stride, void* k_cache, void* v_cache,
+                           const int32_t* num_cached, const int32_t* block_table, int32_t max_blocks_per_seq,
+                           int32_t batch, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                           int32_t num_blocks, int32_t block_size, float softmax_scale, pa_dtype dtype, void* out,
+                           pa_dtype out_dtype, void* workspace, size_t workspace_bytes, void* stream);
+
 /* Keys per split pa_decode uses for these host sizes when split_tokens == 0 and the balanced decode does not
  * apply. */
 int32_t pa_decode_split_tokens(int32_t batch, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,

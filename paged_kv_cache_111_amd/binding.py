@@ -52,6 +52,9 @@ SIGNATURES = {
     "pa_decode": (ctypes.c_int, [_c_ptr, _c_i64, _c_ptr, _c_ptr, _c_ptr, _c_ptr, _c_i32, _c_i32, _c_i32, _c_i32,
                                  _c_i32, _c_i32, _c_i32, _c_f32, ctypes.c_int, _c_ptr, ctypes.c_int, _c_i32, _c_ptr,
                                  _c_size, _c_ptr]),
+    "pa_decode_append": (ctypes.c_int, [_c_ptr, _c_i64, _c_ptr, _c_i64, _c_ptr, _c_i64, _c_ptr, _c_ptr, _c_ptr,
+                                        _c_ptr, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_f32,
+                                        ctypes.c_int, _c_ptr, ctypes.c_int, _c_ptr, _c_size, _c_ptr]),
     "pa_decode_split_tokens": (_c_i32, [_c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32]),
     "pa_decode_workspace_bytes": (_c_size, [_c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32]),
 }
@@ -394,4 +397,45 @@ def decode(q, k_cache, v_cache, context_lens, block_table, softmax_scale: float,
                          hq, hkv, d, nb, bs, float(softmax_scale), _dtype_code(q.dtype), _ptr(out),
                          _dtype_code(out.dtype), int(split_tokens), _ptr(workspace), wbytes, _stream(stream))
     _check("pa_decode", st)
+    return out
+
+
+def decode_append(q, k_new, v_new, k_cache, v_cache, num_cached, block_table, softmax_scale: float, out=None,
+                  out_dtype=torch.float32, workspace=None, fallback=True, stream=None):
+    """pa_decode_append: k_new/v_new [B, Hkv, D] stored at position num_cached[s] of each sequence, then decode
+    over num_cached + 1 keys; returns out [B, Hq, D]. For shapes the fused call does not take, and in checked
+    mode, the same result comes from build_metadata_store followed by decode (with fallback=False an unsupported
+    shape raises instead)."""
+    nb, bs, hkv, d = _cache_dims(k_cache, v_cache)
+    _require(q.dtype == k_cache.dtype and k_new.dtype == k_cache.dtype and v_new.dtype == k_cache.dtype,
+             "q, k_new and v_new must match the cache dtype")
+    hq = int(q.shape[1])
+    qs = _token_rows(q, hq, d, "q")
+    ks = _token_rows(k_new, hkv, d, "k_new")
+    vs = _token_rows(v_new, hkv, d, "v_new")
+    _i32(num_cached, "num_cached")
+    _i32(block_table, "block_table")
+    B = int(q.shape[0])
+    _require(k_new.shape[0] == B and v_new.shape[0] == B and num_cached.shape[0] == B,
+             "q, k_new, v_new and num_cached must have one row per sequence")
+    mbps = int(block_table.shape[1])
+    if out is None:
+        out = torch.empty((B, hq, d), dtype=out_dtype, device=q.device)
+    _require(out.is_contiguous() and tuple(out.shape) == (B, hq, d), "out must be contiguous [B, Hq, D]")
+    need = decode_workspace_bytes(B, hq, hkv, d, mbps, bs, 0)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = PA_ERR_UNSUPPORTED
+    if not checked_mode():
+        st = lib().pa_decode_append(_ptr(q), qs, _ptr(k_new), ks, _ptr(v_new), vs, _ptr(k_cache), _ptr(v_cache),
+                                    _ptr(num_cached), _ptr(block_table), mbps, B, hq, hkv, d, nb, bs,
+                                    float(softmax_scale), _dtype_code(q.dtype), _ptr(out), _dtype_code(out.dtype),
+                                    _ptr(workspace), wbytes, _stream(stream))
+    if st == PA_ERR_UNSUPPORTED and (fallback or checked_mode()):
+        ones = torch.ones(B, dtype=torch.int32, device=q.device)
+        meta = build_metadata_store(num_cached, ones, block_table, B, k_new, v_new, k_cache, v_cache, stream=stream)
+        return decode(q, k_cache, v_cache, meta["context_lens"], block_table, softmax_scale, out=out,
+                      workspace=workspace, stream=stream)
+    _check("pa_decode_append", st)
     return out

@@ -332,4 +332,37 @@ pa_status pa_decode(const void* q, int64_t q_tok_stride, const void* k_cache, co
   return launched();
 }
 
+pa_status pa_decode_append(const void* q, int64_t q_tok_stride, const void* k_new, int64_t k_tok_stride,
+                           const void* v_new, int64_t v_tok_stride, void* k_cache, void* v_cache,
+                           const int32_t* num_cached, const int32_t* block_table, int32_t max_blocks_per_seq,
+                           int32_t batch, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                           int32_t num_blocks, int32_t block_size, float softmax_scale, pa_dtype dtype, void* out,
+                           pa_dtype out_dtype, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!valid_dtype(dtype) || !valid_dtype(out_dtype) || !valid_head_dim(head_dim)) return PA_ERR_UNSUPPORTED;
+  if (batch < 0 || num_heads <= 0 || num_kv_heads <= 0 || num_heads % num_kv_heads != 0 || block_size <= 0 ||
+      num_blocks <= 0)
+    return PA_ERR_SHAPE;
+  if (int64_t(num_blocks) * block_size > kInt32Max) return PA_ERR_SHAPE;
+  const int64_t row = int64_t(num_kv_heads) * head_dim;
+  if (q_tok_stride < int64_t(num_heads) * head_dim || k_tok_stride < row || v_tok_stride < row) return PA_ERR_SHAPE;
+  if (!(softmax_scale > 0.f) || softmax_scale > 3.0e38f) return PA_ERR_SHAPE;
+  if (batch == 0) return PA_OK;
+  if (max_blocks_per_seq <= 0) return PA_ERR_SHAPE;
+  if (!q || !k_new || !v_new || !k_cache || !v_cache || !num_cached || !block_table || !out) return PA_ERR_NULL;
+  if (!decode_uses_mfma(dtype, num_heads, num_kv_heads, head_dim) ||
+      !decode_uses_stream(0, num_heads, num_kv_heads, head_dim, max_blocks_per_seq, block_size, batch))
+    return PA_ERR_UNSUPPORTED;
+  if (q_tok_stride % 8 || k_tok_stride % 8 || v_tok_stride % 8 || !aligned(q, 16) || !aligned(k_new, 16) ||
+      !aligned(v_new, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(out, 16))
+    return PA_ERR_UNSUPPORTED;
+  const size_t need = pa::decode_stream_workspace_bytes(kStreamWorkers);
+  if (workspace_bytes < need) return PA_ERR_WORKSPACE;
+  if (!workspace || !aligned(workspace, 16)) return PA_ERR_NULL;
+  pa::launch_decode_stream(q, q_tok_stride, k_cache, v_cache, num_cached, block_table, max_blocks_per_seq, batch,
+                           num_heads, num_kv_heads, block_size, softmax_scale, out, out_dtype == PA_BF16,
+                           kStreamWorkers, workspace, static_cast<hipStream_t>(stream), k_new, k_tok_stride, v_new,
+                           v_tok_stride);
+  return launched();
+}
+
 }  // extern "C"

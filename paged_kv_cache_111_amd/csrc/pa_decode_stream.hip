@@ -39,8 +39,8 @@ constexpr int kStreamNBuf = PA_STREAM_NBUF;
 // cum[s] = sum over i < s of the lengths rounded up to 32, lens[s] = the length (LDS; batch <= 4096). Each
 // thread sums a run of sequences, the runs are scanned within each wave with shuffles and across the four waves
 // through LDS.
-__device__ __forceinline__ void stream_prefix(const int32_t* __restrict__ ctx_lens, int batch, int32_t* cum,
-                                              int32_t* lens) {
+__device__ __forceinline__ void stream_prefix(const int32_t* __restrict__ ctx_lens, int32_t len_add, int batch,
+                                              int32_t* cum, int32_t* lens) {
   __shared__ int32_t wave_tot[kStreamWaves];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -49,7 +49,7 @@ __device__ __forceinline__ void stream_prefix(const int32_t* __restrict__ ctx_le
   const int lo = min(batch, tid * per), hi = min(batch, lo + per);
   int32_t sum = 0;
   for (int s = lo; s < hi; ++s) {
-    const int32_t L = ctx_lens[s];
+    const int32_t L = ctx_lens[s] + len_add;
     lens[s] = L;
     sum += (L + 31) & ~31;
   }
@@ -115,16 +115,18 @@ __device__ __forceinline__ void load_q_rsrc(bf16x8 (&qb)[4], const uint16_t* qro
 // piece) or 1 (its last).
 template <bool kPow2>
 __global__ __launch_bounds__(64 * kStreamWaves) __attribute__((amdgpu_waves_per_eu(2, 2))) void decode_stream_kernel(
-    const uint16_t* __restrict__ q, int64_t q_stride, const uint16_t* __restrict__ k_cache,
-    const uint16_t* __restrict__ v_cache, const int32_t* __restrict__ ctx_lens,
+    const uint16_t* __restrict__ q, int64_t q_stride, uint16_t* __restrict__ k_cache,
+    uint16_t* __restrict__ v_cache, const int32_t* __restrict__ ctx_lens,
     const int32_t* __restrict__ block_table, int32_t mbps, int32_t batch, int32_t Hq, int32_t Hkv, int32_t bs,
     int32_t bs_shift, float scale_log2, void* __restrict__ out, int out_bf16, float* __restrict__ part,
-    int32_t n_workers) {
+    int32_t n_workers, const uint16_t* __restrict__ k_new, int64_t k_new_stride, const uint16_t* __restrict__ v_new,
+    int64_t v_new_stride) {
   extern __shared__ int32_t smem[];
   int32_t* cum = smem;               // [batch + 1]
   int32_t* lens = smem + batch + 1;  // [batch]
   __shared__ __attribute__((aligned(16))) uint16_t vt_all[kStreamWaves][kDecKeys * kVRow];
-  stream_prefix(ctx_lens, batch, cum, lens);
+  const int32_t len_add = k_new ? 1 : 0;  // appending: ctx_lens holds the cached lengths, the new key comes after
+  stream_prefix(ctx_lens, len_add, batch, cum, lens);
 
   const int64_t Tp = __builtin_amdgcn_readfirstlane(cum[batch]);
   const int64_t total = Tp * Hkv;
@@ -160,6 +162,42 @@ __global__ __launch_bounds__(64 * kStreamWaves) __attribute__((amdgpu_waves_per_
     cc.Lp = (cc.L + 31) & ~31;
   }
   StreamCursor lc = cc;  // the next tile to load
+
+  if (k_new) {
+    // Appending: the new token of a pair is its last key, and only the worker whose slice holds that key reads
+    // its row, so that worker writes the pair's head of the new K and V rows to their slot before its first
+    // tile loads (lanes 0-15: 16 bytes of K each, lanes 16-31: of V). Pairs overlapping the slice are walked
+    // from its first one.
+    StreamCursor pc = cc;
+    int64_t pu = u0 - pc.t;  // where the current pair starts
+    for (int it = 0; it <= batch * Hkv; ++it) {
+      const int64_t last = pu + pc.L - 1;
+      if (last >= u0 && last < u1 && lane < 32) {
+        const int pos = pc.L - 1;
+        const int blk = kPow2 ? (pos >> bs_shift) : (pos / bs);
+        const int64_t slot = int64_t(block_table[int64_t(pc.s) * mbps + blk]) * bs + (pos - blk * bs);
+        if (slot >= 0) {
+          const bool is_v = lane >= 16;
+          const int64_t e = int64_t(pc.h) * 128 + 8 * (lane & 15);
+          const u32x4 x = *reinterpret_cast<const u32x4*>(
+              is_v ? v_new + int64_t(pc.s) * v_new_stride + e : k_new + int64_t(pc.s) * k_new_stride + e);
+          *reinterpret_cast<u32x4*>((is_v ? v_cache : k_cache) + slot * (int64_t(Hkv) * 128) + e) = x;
+        }
+      }
+      pu += pc.Lp;
+      if (pu >= u1) break;
+      for (int k = 0; k < batch; ++k) {  // the next pair with keys
+        if (++pc.s == batch) {
+          pc.s = 0;
+          ++pc.h;
+        }
+        pc.L = __builtin_amdgcn_readfirstlane(lens[pc.s]);
+        pc.Lp = (pc.L + 31) & ~31;
+        if (pc.Lp > 0) break;
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "workgroup");  // the rows are written before this wave reads them
+  }
 
   auto qrow = [&](const StreamCursor& c) { return q + int64_t(c.s) * q_stride + int64_t(c.h * G) * 128; };
   // Loads the tile at lc; a tile index past the slice gets a zero-sized descriptor at lc's (real) tile.
@@ -260,10 +298,11 @@ __global__ __launch_bounds__(64 * kStreamWaves) __attribute__((amdgpu_waves_per_
 // rows are read eight at a time.
 constexpr int kMergeEager = 8;
 
-__global__ __launch_bounds__(64) void decode_stream_merge_kernel(const int32_t* __restrict__ ctx_lens, int32_t batch,
-                                                                 int32_t Hq, int32_t Hkv,
-                                                                 const float* __restrict__ part, int32_t n_workers,
-                                                                 void* __restrict__ out, int out_bf16) {
+__global__ __launch_bounds__(64) void decode_stream_merge_kernel(const int32_t* __restrict__ ctx_lens,
+                                                                 int32_t len_add, int32_t batch, int32_t Hq,
+                                                                 int32_t Hkv, const float* __restrict__ part,
+                                                                 int32_t n_workers, void* __restrict__ out,
+                                                                 int out_bf16) {
   const int G = Hq / Hkv;
   const int h = int(blockIdx.x) / G;
   const int g = int(blockIdx.x) - h * G;
@@ -271,7 +310,7 @@ __global__ __launch_bounds__(64) void decode_stream_merge_kernel(const int32_t* 
   const int lane = threadIdx.x;
   int64_t before = 0, all = 0;
   for (int i = lane; i < batch; i += 64) {
-    const int32_t Lp = (ctx_lens[i] + 31) & ~31;
+    const int32_t Lp = (ctx_lens[i] + len_add + 31) & ~31;
     all += Lp;
     if (i < s) before += Lp;
   }
@@ -282,7 +321,7 @@ __global__ __launch_bounds__(64) void decode_stream_merge_kernel(const int32_t* 
   const int64_t total = all * Hkv;
   const int64_t chunk = stream_chunk(total, n_workers);
   const int64_t a = int64_t(h) * all + before;
-  const int64_t b = a + ((ctx_lens[s] + 31) & ~31);
+  const int64_t b = a + ((ctx_lens[s] + len_add + 31) & ~31);
   if (b == a) return;  // no keys (lengths are documented >= 1)
   const int w0 = int(a / chunk);
   const int w1 = int((b - 1) / chunk);
@@ -353,7 +392,8 @@ size_t decode_stream_workspace_bytes(int32_t n_workers) {
 void launch_decode_stream(const void* q, int64_t q_stride, const void* k_cache, const void* v_cache,
                           const int32_t* ctx_lens, const int32_t* block_table, int32_t mbps, int32_t batch,
                           int32_t Hq, int32_t Hkv, int32_t block_size, float scale, void* out, bool out_bf16,
-                          int32_t n_workers, void* workspace, hipStream_t stream) {
+                          int32_t n_workers, void* workspace, hipStream_t stream, const void* k_new,
+                          int64_t k_new_stride, const void* v_new, int64_t v_new_stride) {
   float* part = static_cast<float*>(workspace);
   const float sl2 = scale * kLog2e;
   const bool pow2 = (block_size & (block_size - 1)) == 0;
@@ -362,19 +402,22 @@ void launch_decode_stream(const void* q, int64_t q_stride, const void* k_cache, 
   const size_t lds = size_t(2 * batch + 1) * sizeof(int32_t);
   const dim3 grid(unsigned((n_workers + kStreamWaves - 1) / kStreamWaves));
   const uint16_t* qp = static_cast<const uint16_t*>(q);
-  const uint16_t* kc = static_cast<const uint16_t*>(k_cache);
-  const uint16_t* vc = static_cast<const uint16_t*>(v_cache);
+  // the caches are written only when appending (k_new given); pa_decode passes them as read-only
+  uint16_t* kc = static_cast<uint16_t*>(const_cast<void*>(k_cache));
+  uint16_t* vc = static_cast<uint16_t*>(const_cast<void*>(v_cache));
+  const uint16_t* kn = static_cast<const uint16_t*>(k_new);
+  const uint16_t* vn = static_cast<const uint16_t*>(v_new);
   if (pow2) {
     hipLaunchKernelGGL(decode_stream_kernel<true>, grid, dim3(64 * kStreamWaves), lds, stream, qp, q_stride, kc, vc,
                        ctx_lens, block_table, mbps, batch, Hq, Hkv, block_size, shift, sl2, out, int(out_bf16), part,
-                       n_workers);
+                       n_workers, kn, k_new_stride, vn, v_new_stride);
   } else {
     hipLaunchKernelGGL(decode_stream_kernel<false>, grid, dim3(64 * kStreamWaves), lds, stream, qp, q_stride, kc,
                        vc, ctx_lens, block_table, mbps, batch, Hq, Hkv, block_size, shift, sl2, out, int(out_bf16),
-                       part, n_workers);
+                       part, n_workers, kn, k_new_stride, vn, v_new_stride);
   }
-  hipLaunchKernelGGL(decode_stream_merge_kernel, dim3(Hq, batch), dim3(64), 0, stream, ctx_lens, batch, Hq, Hkv,
-                     part, n_workers, out, int(out_bf16));
+  hipLaunchKernelGGL(decode_stream_merge_kernel, dim3(Hq, batch), dim3(64), 0, stream, ctx_lens,
+                     int32_t(k_new ? 1 : 0), batch, Hq, Hkv, part, n_workers, out, int(out_bf16));
 }
 
 }  // namespace pa

@@ -51,7 +51,8 @@ size_t decode_stream_workspace_bytes(int32_t n_workers);
 void launch_decode_stream(const void* q, int64_t q_stride, const void* k_cache, const void* v_cache,
                           const int32_t* ctx_lens, const int32_t* block_table, int32_t mbps, int32_t batch,
                           int32_t Hq, int32_t Hkv, int32_t block_size, float scale, void* out, bool out_bf16,
-                          int32_t n_workers, void* workspace, hipStream_t stream);
+                          int32_t n_workers, void* workspace, hipStream_t stream, const void* k_new = nullptr,
+                          int64_t k_new_stride = 0, const void* v_new = nullptr, int64_t v_new_stride = 0);
 
 void launch_prefill_mfma(const void* q, int64_t q_stride, const void* k_cache, const void* v_cache,
                          const int32_t* cu_q, const int32_t* cu_k, const int32_t* block_table, int32_t mbps,

@@ -53,9 +53,16 @@ class DevStep:
 
 
 def hip_step(wl, ds: DevStep, kc: torch.Tensor, vc: torch.Tensor, out_dtype=torch.float32, split_tokens=0,
-             fused_store=False):
-    """The whole path on the GPU: metadata, store, attention (metadata and store in one launch with fused_store).
-    Returns (metadata tensors, output tensor)."""
+             fused_store=False, append=False):
+    """The whole path on the GPU: metadata, store, attention (metadata and store in one launch with fused_store;
+    with append, a decode step stores and attends in pa_decode_append and the metadata call only computes the
+    arrays compared with the oracle's). Returns (metadata tensors, output tensor)."""
+    if append and ds.step.kind == "decode":
+        meta = pa.build_metadata(ds.num_cached, ds.num_new, ds.block_table, ds.total_q, wl.num_blocks,
+                                 wl.block_size)
+        out = pa.decode_append(ds.q, ds.k, ds.v, kc, vc, ds.num_cached, ds.block_table, wl.scale,
+                               out_dtype=out_dtype, fallback=False)
+        return meta, out
     if fused_store:
         meta = pa.build_metadata_store(ds.num_cached, ds.num_new, ds.block_table, ds.total_q, ds.k, ds.v, kc, vc)
     else:

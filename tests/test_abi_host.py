@@ -152,6 +152,34 @@ def test_decode_rejects_bad_arguments():
     assert _decode(bs=-4) == b.PA_ERR_SHAPE
 
 
+def _append(**kw):
+    args = dict(q=NULL, qs=64 * 128, kn=NULL, ks=8 * 128, vn=NULL, vs=8 * 128, kc=NULL, vc=NULL, nc=NULL, bt=NULL,
+                mbps=128, batch=256, hq=64, hkv=8, d=128, nb=10000, bs=256, scale=0.1, dtype=1, out=NULL, odt=0,
+                ws=NULL, wsb=0, st=NULL)
+    args.update(kw)
+    return pa.lib().pa_decode_append(*args.values())
+
+
+def test_decode_append_rejects_bad_arguments():
+    fake = ctypes.c_void_p(1 << 20)       # never dereferenced: every call below returns before a launch
+    ptrs = dict(q=fake, kn=fake, vn=fake, kc=fake, vc=fake, nc=fake, bt=fake, out=fake)
+    assert _append() == b.PA_ERR_NULL
+    assert _append(batch=0) == b.PA_OK
+    assert _append(hq=60) == b.PA_ERR_SHAPE
+    assert _append(ks=8 * 128 - 8) == b.PA_ERR_SHAPE   # token stride shorter than Hkv*D
+    assert _append(dtype=5) == b.PA_ERR_UNSUPPORTED
+    assert _append(scale=0.0) == b.PA_ERR_SHAPE
+    # shapes the balanced decode does not take: unsupported, so the caller stores and decodes separately
+    assert _append(bs=16, **ptrs) == b.PA_ERR_UNSUPPORTED
+    assert _append(dtype=0, **ptrs) == b.PA_ERR_UNSUPPORTED          # fp16: the vector decode
+    assert _append(hq=256, qs=256 * 128, **ptrs) == b.PA_ERR_UNSUPPORTED    # 32 query heads per KV head
+    assert _append(batch=5000, **ptrs) == b.PA_ERR_UNSUPPORTED
+    assert _append(vs=8 * 128 + 4, **ptrs) == b.PA_ERR_UNSUPPORTED   # not a multiple of 8 elements
+    need = pa.decode_workspace_bytes(256, 64, 8, 128, 128, 256, 0)
+    assert _append(wsb=need - 1, **ptrs) == b.PA_ERR_WORKSPACE
+    assert _append(wsb=need, **ptrs) == b.PA_ERR_NULL                # workspace pointer missing
+
+
 def test_decode_workspace_query():
     # one split covers the whole table: no workspace
     assert pa.decode_workspace_bytes(64, 16, 8, 128, 16, 256, 4096) == 0

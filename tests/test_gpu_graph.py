@@ -141,3 +141,57 @@ def test_graph_fused_metadata_store_decode_replays(batch):
             assert torch.equal(meta_g[key], meta_e[key]), f"replay {r}: {key} differs"
         assert torch.equal(out_g, out_e), f"replay {r}: graph output differs from the eager calls"
         assert torch.equal(kc_g, kc_e) and torch.equal(vc_g, vc_e), f"replay {r}: caches differ"
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("batch", [1, 8, 64])
+def test_graph_decode_append_replays(batch):
+    """pa_decode_append (slots from the table, store and attention in the decode's two launches) captured once and
+    replayed with new cached lengths, queries and K/V; each replay must equal, bit for bit, the metadata + store
+    launch followed by pa_decode run eagerly on a second pool (the same arithmetic over the same lengths)."""
+    rng = np.random.default_rng(970 + batch)
+    mbps = 8
+    nb = batch * mbps + 4
+    perm = rng.permutation(nb).astype(np.int32)
+    table = perm[: batch * mbps].reshape(batch, mbps)
+    kc_g, vc_g = _bf16(rng, (nb, BS, HKV, D)).to(DEV), _bf16(rng, (nb, BS, HKV, D)).to(DEV)
+    kc_e, vc_e = kc_g.clone(), vc_g.clone()
+
+    q = torch.empty((batch, HQ, D), dtype=torch.bfloat16, device=DEV)
+    k_new = torch.empty((batch, HKV, D), dtype=torch.bfloat16, device=DEV)
+    v_new = torch.empty_like(k_new)
+    num_cached = torch.empty(batch, dtype=torch.int32, device=DEV)
+    num_new = torch.ones(batch, dtype=torch.int32, device=DEV)
+    bt = torch.from_numpy(table).to(DEV)
+    out_g = torch.empty((batch, HQ, D), dtype=torch.float32, device=DEV)
+    out_e = torch.empty_like(out_g)
+    need = pa.decode_workspace_bytes(batch, HQ, HKV, D, mbps, BS, 0)
+    ws_g = torch.empty(max(need, 16), dtype=torch.uint8, device=DEV)
+    ws_e = torch.empty_like(ws_g)
+    scale = 1.0 / np.sqrt(D)
+
+    def draw():
+        cached = rng.integers(0, mbps * BS, size=batch).astype(np.int32)
+        q.copy_(_bf16(rng, (batch, HQ, D)).to(DEV))
+        k_new.copy_(_bf16(rng, (batch, HKV, D)).to(DEV))
+        v_new.copy_(_bf16(rng, (batch, HKV, D)).to(DEV))
+        num_cached.copy_(torch.from_numpy(cached).to(DEV))
+        torch.cuda.synchronize()
+
+    draw()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        pa.decode_append(q, k_new, v_new, kc_g, vc_g, num_cached, bt, scale, out=out_g, workspace=ws_g,
+                         fallback=False)
+    torch.cuda.synchronize()
+    for r in range(4):
+        if r > 0:
+            draw()
+        g.replay()
+        torch.cuda.synchronize()
+        meta = pa.build_metadata_store(num_cached, num_new, bt, batch, k_new, v_new, kc_e, vc_e)
+        pa.decode(q, kc_e, vc_e, meta["context_lens"], bt, scale, out=out_e, workspace=ws_e)
+        torch.cuda.synchronize()
+        assert torch.isfinite(out_e).all(), f"replay {r}: eager output not finite"
+        assert torch.equal(out_g, out_e), f"replay {r}: graph output differs from store + decode"
+        assert torch.equal(kc_g, kc_e) and torch.equal(vc_g, vc_e), f"replay {r}: caches differ"

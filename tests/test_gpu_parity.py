@@ -18,7 +18,7 @@ pytestmark = pytest.mark.gpu
 
 
 def _run_and_check(wl, out_dtype=torch.float32, split_tokens=0, seqs=None, rows=None, check_pool=True,
-                   fused_store=False):
+                   fused_store=False, append=False):
     """Every step of the workload on both sides; returns the per-step (max_abs, rel_rms)."""
     kc_h, vc_h = wl.k_cache.copy(), wl.v_cache.copy()
     kc, vc = to_dev(wl.k_cache, wl.dtype), to_dev(wl.v_cache, wl.dtype)
@@ -27,7 +27,7 @@ def _run_and_check(wl, out_dtype=torch.float32, split_tokens=0, seqs=None, rows=
         print(f"[case] {wl.name} step {i} {step.kind} B={step.batch} T={step.num_tokens}", flush=True)
         ds = DevStep(step, wl.dtype)
         meta_d, out = hip_step(wl, ds, kc, vc, out_dtype=out_dtype, split_tokens=split_tokens,
-                               fused_store=fused_store)
+                               fused_store=fused_store, append=append)
         torch.cuda.synchronize()
         meta_r, ref = oracle_step(wl, step, kc_h, vc_h, seqs=seqs, rows=rows)
         compare_metadata(meta_d, meta_r)
@@ -67,8 +67,10 @@ def decode_32b():
     return make_config("decode_qwen3_32b")
 
 
-def test_decode_qwen3_32b_config_sampled(decode_32b):
-    """Full-size pool (offsets beyond 2^31 elements); the oracle checks 16 sequences, the store every slot."""
+@pytest.mark.parametrize("append", [False, True])
+def test_decode_qwen3_32b_config_sampled(decode_32b, append):
+    """Full-size pool (offsets beyond 2^31 elements); the oracle checks 16 sequences, the store every slot (with
+    append, the store is the decode call's own)."""
     wl = decode_32b
     step = wl.steps[0]
     ctx = step.num_cached + 1
@@ -77,11 +79,11 @@ def test_decode_qwen3_32b_config_sampled(decode_32b):
     rng = np.random.default_rng(7)
     pick |= set(rng.choice(step.batch, 10, replace=False).tolist())
     seqs = sorted(pick)
-    print(f"[case] decode_qwen3_32b seqs {seqs}", flush=True)
+    print(f"[case] decode_qwen3_32b append={append} seqs {seqs}", flush=True)
     kc, vc = to_dev(wl.k_cache, wl.dtype), to_dev(wl.v_cache, wl.dtype)
     kc0 = kc.clone()
     ds = DevStep(step, wl.dtype)
-    meta_d, out = hip_step(wl, ds, kc, vc)
+    meta_d, out = hip_step(wl, ds, kc, vc, append=append)
     torch.cuda.synchronize()
     meta_r, ref = oracle_step(wl, step, wl.k_cache, wl.v_cache, seqs=seqs)  # idempotent store into the fixture
     compare_metadata(meta_d, meta_r)
@@ -90,8 +92,9 @@ def test_decode_qwen3_32b_config_sampled(decode_32b):
     changed = torch.nonzero((kc.view(-1, row) != kc0.view(-1, row)).any(dim=1)).flatten().cpu().numpy()
     slots = meta_r["slot_mapping"]
     assert set(changed.tolist()) <= set(slots.tolist())
-    got_rows = to_host_bits(kc.view(-1, row)[torch.from_numpy(slots.astype(np.int64)).to(DEV)])
-    assert np.array_equal(got_rows, step.k.reshape(step.batch, row))
+    idx = torch.from_numpy(slots.astype(np.int64)).to(DEV)
+    assert np.array_equal(to_host_bits(kc.view(-1, row)[idx]), step.k.reshape(step.batch, row))
+    assert np.array_equal(to_host_bits(vc.view(-1, row)[idx]), step.v.reshape(step.batch, row))
     del kc0
     assert_close(out, ref, flat_rows(meta_r, seqs), what="decode_qwen3_32b")
 
@@ -183,6 +186,48 @@ def test_decode_largest_batch():
     ctx = [int(x) for x in np.random.default_rng(11).integers(1, 65, 4096)]
     wl = build_decode("decode_4096", 620, 8, 2, 128, 32, "bf16", ctx, num_blocks=sum(-(-n // 32) for n in ctx) + 2)
     _run_and_check(wl)
+
+
+# the decode step with the new K/V given (pa_decode_append: store inside the balanced decode's pass) on every
+# decode shape it takes: 1..20000 keys, block sizes 32 to 256, G = 2 to 16, 300 and 4096 sequences, the
+# Qwen3-0.6B workload's steps; the caches must match the oracle's bit for bit after each step
+APPEND_CASES = [0, 8, 9, 10]
+
+
+@pytest.mark.parametrize("case", APPEND_CASES)
+def test_decode_append(case):
+    Hq, Hkv, D, bs, dt, ctx, _ = DECODE_CASES[case]
+    wl = build_decode(f"append_decode_{case}", 300 + case, Hq, Hkv, D, bs, dt, ctx,
+                      num_blocks=sum(-(-n // bs) for n in ctx) + 2)
+    _run_and_check(wl, append=True)
+
+
+def test_decode_append_qwen3_0p6b_config_and_largest_batch():
+    _run_and_check(make_config("decode_qwen3_0p6b"), append=True)
+    ctx = [int(x) for x in np.random.default_rng(11).integers(1, 65, 4096)]
+    wl = build_decode("append_decode_4096", 620, 8, 2, 128, 32, "bf16", ctx,
+                      num_blocks=sum(-(-n // 32) for n in ctx) + 2)
+    _run_and_check(wl, append=True, out_dtype=torch.bfloat16)
+
+
+@pytest.mark.parametrize("case", [3, 6, 12])
+def test_decode_append_falls_back_on_other_shapes(case):
+    """Block size 16, float32, 32 query heads per KV head: the binding stores and decodes in separate calls."""
+    Hq, Hkv, D, bs, dt, ctx, _ = DECODE_CASES[case]
+    wl = build_decode(f"append_fallback_{case}", 300 + case, Hq, Hkv, D, bs, dt, ctx,
+                      num_blocks=sum(-(-n // bs) for n in ctx) + 2)
+    ds = DevStep(wl.steps[0], wl.dtype)
+    kc, vc = to_dev(wl.k_cache, wl.dtype), to_dev(wl.v_cache, wl.dtype)
+    with pytest.raises(RuntimeError, match="UNSUPPORTED"):
+        pa.decode_append(ds.q, ds.k, ds.v, kc, vc, ds.num_cached, ds.block_table, wl.scale, fallback=False)
+    kc_h, vc_h = wl.k_cache.copy(), wl.v_cache.copy()
+    for i, step in enumerate(wl.steps):
+        ds = DevStep(step, wl.dtype)
+        out = pa.decode_append(ds.q, ds.k, ds.v, kc, vc, ds.num_cached, ds.block_table, wl.scale)
+        torch.cuda.synchronize()
+        _, ref = oracle_step(wl, step, kc_h, vc_h)
+        assert np.array_equal(to_host_bits(kc), kc_h) and np.array_equal(to_host_bits(vc), vc_h)
+        assert_close(out, ref, what=f"fallback {case} step {i}")
 
 
 # metadata and store in one launch (pa_build_metadata_store) on shapes of the cases above: bf16 and f32 rows of
