@@ -23,6 +23,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -80,11 +81,19 @@ ATTN_SOURCES = {"decode": ("pa_decode_stream.hip", "pa_decode_tile.h", "pa_commo
 ATTN_KERNELS = {"decode": ("decode_stream_kernel", "decode_stream_merge_kernel"), "prefill": ("prefill_mfma_kernel",)}
 
 
+def _code_text(src: str) -> str:
+    """A source file without its comments, trailing spaces and blank lines: what a counter summary is tied to
+    (a change of wording in a comment does not make the measured kernels stale)."""
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    lines = (re.sub(r"//.*", "", ln).rstrip() for ln in src.splitlines())
+    return "\n".join(ln for ln in lines if ln)
+
+
 def _src_sha(*names) -> str:
     h = hashlib.sha256()
     for n in names:
-        with open(os.path.join(ROOT, "paged_kv_cache_111_amd", "csrc", n), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, "paged_kv_cache_111_amd", "csrc", n), encoding="utf-8") as f:
+            h.update(_code_text(f.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -10,6 +10,12 @@
 // slice's ends leaves an unnormalised partial (m, l, O) in one of the worker's two slots, and the merge pass
 // combines the partials of each cut pair with the log-sum-exp rule.
 //
+// Appending (the new token's K and V given with the cached lengths): each pair's length is its cached length plus
+// one, and its new key is the last one. The worker whose slice holds that key, and no other, reads the key's
+// tile, so before its first load it writes that head's piece of the new K and V rows to the key's slot (found in
+// the block table) and then reads it back with the tile: the store and the attention of a decode step take the
+// same two launches as the attention alone.
+//
 // Against a split of fixed size per sequence, this removes both the finishing imbalance of long splits on mixed
 // lengths and the per-wave fixed costs of short ones. The per-tile work (32-key tiles of K and V through buffer
 // descriptors, 16x16x32 bf16 MFMAs for scores and PV, online softmax) is the split kernel's.

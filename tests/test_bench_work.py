@@ -64,3 +64,11 @@ def test_bench_refuses_more_than_one_gpu():
     assert r.returncode == 2
     assert "one GPU" in r.stderr
     assert r.stdout == ""
+
+
+def test_source_hash_ignores_comments_only():
+    a = "int f(int x) {  // doubles x\n  return 2 * x;\n}\n/* block\n comment */\n"
+    b = "// a new header line\nint f(int x) {  // twice x\n\n  return 2 * x;   \n}\n"
+    c = "int f(int x) {\n  return 3 * x;\n}\n"
+    assert bench._code_text(a) == bench._code_text(b)
+    assert bench._code_text(a) != bench._code_text(c)
