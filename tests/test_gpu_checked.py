@@ -177,3 +177,32 @@ def test_checked_mode_raises_before_launching(monkeypatch):
     kept = (rows != 5) & (rows != 7)      # the two rows of the valid store above
     assert torch.equal(kc.view(NB * BS, Hkv, D)[kept], kc0.view(NB * BS, Hkv, D)[kept])
     assert torch.equal(kc.view(NB * BS, Hkv, D)[7], k[2])
+
+
+def test_checked_mode_decode_append(monkeypatch):
+    """pa_decode_append in checked mode: the binding validates the metadata and lengths it derives, so a table
+    whose entry for the new token is out of range raises before anything is stored or computed."""
+    monkeypatch.setenv("PA_CHECKED", "1")
+    rng = np.random.default_rng(5)
+    Hq, Hkv, D = 4, 2, 128
+    bs = 32
+    nb = 20
+    kc = torch.from_numpy(rng.standard_normal((nb, bs, Hkv, D), dtype=np.float32)).to(DEV).bfloat16()
+    vc = kc.clone()
+    kc0 = kc.clone()
+    table = np.arange(2 * 4, dtype=np.int32).reshape(2, 4)
+    table[1, 2] = nb + 1                      # the block of sequence 1's new token (position 70)
+    q = torch.ones((2, Hq, D), dtype=torch.bfloat16, device=DEV)
+    k_new = torch.full((2, Hkv, D), 3.0, dtype=torch.bfloat16, device=DEV)
+    out = torch.full((2, Hq, D), 7.0, device=DEV)
+    with pytest.raises(pa.PAIndexError):
+        pa.decode_append(q, k_new, k_new, kc, vc, i32([10, 70]), i32(table), 0.1, out=out)
+    torch.cuda.synchronize()
+    assert torch.equal(kc, kc0) and bool((out == 7.0).all())
+    # the same call with a valid table stores both rows and computes the output
+    table[1, 2] = 9
+    pa.decode_append(q, k_new, k_new, kc, vc, i32([10, 70]), i32(table), 0.1, out=out)
+    torch.cuda.synchronize()
+    flat = kc.view(nb * bs, Hkv, D)
+    assert torch.equal(flat[table[0, 0] * bs + 10], k_new[0]) and torch.equal(flat[9 * bs + 70 - 64], k_new[1])
+    assert torch.isfinite(out).all()
