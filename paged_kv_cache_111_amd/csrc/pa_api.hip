@@ -58,13 +58,14 @@ bool decode_uses_mfma(pa_dtype dtype, int32_t Hq, int32_t Hkv, int32_t D) {
 constexpr int32_t kStreamWorkers = PA_STREAM_WORKERS;
 
 // The balanced decode takes split_tokens == 0 when its kernel fits the sizes: D = 128, at most 16 query heads per
-// KV head (one partial slot holds 16 rows), 32-key tiles inside a block, a batch whose prefix sums fit in LDS
-// (4096 sequences), and padded lengths whose sum over the batch fits the int32 prefix sums.
+// KV head (one partial slot holds 16 rows), at least one worker per KV head, 32-key tiles inside a block, a batch
+// whose prefix sums fit in LDS (4096 sequences), and padded lengths whose sum over the batch fits the int32
+// prefix sums.
 bool decode_uses_stream(int32_t split_tokens, int32_t Hq, int32_t Hkv, int32_t D, int32_t mbps, int32_t block_size,
                         int32_t batch) {
   const int64_t padded_max = (int64_t(mbps) * block_size + 31) & ~int64_t(31);
-  return split_tokens == 0 && D == 128 && Hq / Hkv <= 16 && block_size % 32 == 0 && batch <= 4096 &&
-         int64_t(batch) * padded_max < (int64_t(1) << 31);
+  return split_tokens == 0 && D == 128 && Hq / Hkv <= 16 && Hkv <= kStreamWorkers && block_size % 32 == 0 &&
+         batch <= 4096 && int64_t(batch) * padded_max < (int64_t(1) << 31);
 }
 
 }  // namespace
