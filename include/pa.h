@@ -247,9 +247,8 @@ pa_status pa_decode(const void* q, int64_t q_tok_stride, const void* k_cache, co
  * The same as pa_store_kvcache of k_new[s], v_new[s] at position num_cached[s] of sequence s (slot
  * block_table[s][pos / block_size] * block_size + pos % block_size, pos = num_cached[s]) followed by pa_decode
  * over context_lens[s] = num_cached[s] + 1 keys, in the balanced decode's two launches (instead of the metadata
- * and store launches followed by those two): the
- * worker whose slice holds a pair's new key writes that head of the new rows and then reads them as part of its
- * slice. FlashAttention's decode call takes the new k, v the same way and updates the cache in place ("Nano-vLLM
+ * and store launches followed by those two): the worker whose slice holds a pair's new key writes that head of
+ * the new rows and then reads them as part of its slice. FlashAttention's decode call takes the new k, v the same way and updates the cache in place ("Nano-vLLM
  * 架构详解" §3.2, flash_attn_with_kvcache; the step is store then attention, "一个 prompt 的一生" §4).
  *   q      (device) [batch, num_heads, head_dim]; k_new, v_new (device) [batch, num_kv_heads, head_dim], token
  *          stride *_tok_stride elements (a multiple of 8), 16-byte aligned
