@@ -14,7 +14,8 @@ step reads was not touched by the previous few steps and cannot sit in the 256 M
 Printed: one JSON line with the whole-step throughput (`value`, GB/s of algorithmic bytes over the wall time of
 K uninstrumented steps), the roofline of the decode attention call (its duration from HIP events recorded on
 the launch stream in a second pass of K steps), the oracle's CPU throughput on a bounded sample, and secondary
-entries for the prefill and long-context decode workloads.
+entries for the prefill workloads (varlen, a 2048-row chunk and a 256-row chunk over a long prefix) and the
+long-context decode workload.
 """
 
 from __future__ import annotations
@@ -714,7 +715,7 @@ def main() -> int:
     print(f"[bench] {main_name}: {json.dumps(main['timing'])}", file=sys.stderr, flush=True)
     secondary = []
     if not args.only and not args.no_secondary:
-        for name in ("prefill_qwen3_8b", "chunked_qwen3_8b", "decode_qwen3_32b"):
+        for name in ("prefill_qwen3_8b", "chunked_qwen3_8b", "chunk256_qwen3_8b", "decode_qwen3_32b"):
             layers = 1 if name == "decode_qwen3_32b" else args.layers
             _, r = bench_one(name, max(10, args.steps // 2), max(2, args.warmup // 2), layers, args.out_dtype,
                              fused, append)

@@ -205,6 +205,11 @@ pa_status pa_norm_rope_store_kvcache(const void* k, int64_t k_tok_stride, const 
  *   max_seqlen_q (host) >= every q_len; max_seqlen_k (host) >= every k_len (sizes the grid)
  *   out          (device) [total_q, num_heads, head_dim], contiguous, out_dtype
  *   workspace    (device) at least pa_prefill_workspace_bytes(...) bytes (may be NULL when that is 0)
+ * With few query tiles over long keys (a small chunk after a long cached prefix, as in chunked prefill: fewer
+ * 128-row tiles times heads than the chip runs at once), the bf16 head_dim-128 kernel splits each tile's keys into
+ * up to 32 ranges of at least 1024 keys, chosen from the host sizes alone, and a second launch merges the
+ * ranges' partial results with the log-sum-exp rule; the workspace then holds those partials (scratch: its
+ * contents do not matter between calls). Results agree to rounding with and without splits.
  */
 pa_status pa_prefill_varlen(const void* q, int64_t q_tok_stride, const void* k_cache, const void* v_cache,
                             const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, const int32_t* block_table,
@@ -213,7 +218,8 @@ pa_status pa_prefill_varlen(const void* q, int64_t q_tok_stride, const void* k_c
                             int32_t num_blocks, int32_t block_size, float softmax_scale, pa_dtype dtype,
                             void* out, pa_dtype out_dtype, void* workspace, size_t workspace_bytes, void* stream);
 
-/* Workspace bytes pa_prefill_varlen needs for these host sizes (currently always 0). */
+/* Workspace bytes pa_prefill_varlen needs for these host sizes: 0 unless the call splits its keys (then
+ * batch * ceil(max_seqlen_q / 128) * num_heads * splits * 128 rows of 132 floats). */
 size_t pa_prefill_workspace_bytes(int32_t batch, int32_t num_heads, int32_t head_dim, int32_t max_seqlen_q,
                                   int32_t max_seqlen_k);
 

@@ -227,8 +227,9 @@ pa_status pa_sample(const float* logits, int64_t row_stride, const float* temper
 
 size_t pa_prefill_workspace_bytes(int32_t batch, int32_t num_heads, int32_t head_dim, int32_t max_seqlen_q,
                                   int32_t max_seqlen_k) {
-  (void)batch; (void)num_heads; (void)head_dim; (void)max_seqlen_q; (void)max_seqlen_k;
-  return 0;
+  // only the matrix-core kernel (head_dim 128) uses a workspace: the partials of its key splits
+  if (batch <= 0 || num_heads <= 0 || head_dim != 128 || max_seqlen_q <= 0 || max_seqlen_k <= 0) return 0;
+  return pa::prefill_mfma_workspace_bytes(batch, max_seqlen_q, max_seqlen_k, num_heads);
 }
 
 pa_status pa_prefill_varlen(const void* q, int64_t q_tok_stride, const void* k_cache, const void* v_cache,
@@ -255,9 +256,11 @@ pa_status pa_prefill_varlen(const void* q, int64_t q_tok_stride, const void* k_c
   const bool mfma = dtype == PA_BF16 && head_dim == 128 && q_tok_stride % 8 == 0 && aligned(q, 16) &&
                     aligned(k_cache, 16) && aligned(v_cache, 16) && aligned(out, 16);
   if (mfma) {
+    if (pa::prefill_splits(batch, max_seqlen_q, max_seqlen_k, num_heads) > 1 && (!workspace || !aligned(workspace, 16)))
+      return PA_ERR_NULL;
     pa::launch_prefill_mfma(q, q_tok_stride, k_cache, v_cache, cu_seqlens_q, cu_seqlens_k, block_table,
-                            max_blocks_per_seq, batch, max_seqlen_q, num_heads, num_kv_heads, block_size,
-                            softmax_scale, out, out_bf16, st);
+                            max_blocks_per_seq, batch, total_q, max_seqlen_q, max_seqlen_k, num_heads, num_kv_heads,
+                            block_size, softmax_scale, out, out_bf16, workspace, st);
   } else {
     pa::launch_attn_generic(dtype == PA_BF16, q, q_tok_stride, k_cache, v_cache, cu_seqlens_q, cu_seqlens_k,
                             nullptr, block_table, max_blocks_per_seq, batch, total_q, num_heads, num_kv_heads,

@@ -56,8 +56,12 @@ void launch_decode_stream(const void* q, int64_t q_stride, const void* k_cache, 
 
 void launch_prefill_mfma(const void* q, int64_t q_stride, const void* k_cache, const void* v_cache,
                          const int32_t* cu_q, const int32_t* cu_k, const int32_t* block_table, int32_t mbps,
-                         int32_t batch, int32_t max_seqlen_q, int32_t Hq, int32_t Hkv, int32_t block_size,
-                         float scale, void* out, bool out_bf16, hipStream_t stream);
+                         int32_t batch, int32_t total_q, int32_t max_seqlen_q, int32_t max_seqlen_k, int32_t Hq,
+                         int32_t Hkv, int32_t block_size, float scale, void* out, bool out_bf16, void* workspace,
+                         hipStream_t stream);
+// Key splits the prefill kernel uses for these host sizes, and the workspace its partials need (0 for one split).
+int32_t prefill_splits(int32_t batch, int32_t max_seqlen_q, int32_t max_seqlen_k, int32_t Hq);
+size_t prefill_mfma_workspace_bytes(int32_t batch, int32_t max_seqlen_q, int32_t max_seqlen_k, int32_t Hq);
 
 
 }  // namespace pa

@@ -22,6 +22,7 @@
 // query head in the group). The G query heads that share a KV head, and the query tiles of that head, then run
 // on one XCD and read the same K/V through its L2; the last (heaviest, under the causal mask) query tiles of
 // all sequences start first, so the short tail of light tiles balances the finish.
+#include <algorithm>
 #include <type_traits>
 
 #include "pa_prefill_tile.h"
@@ -29,20 +30,24 @@
 namespace pa {
 
 constexpr int kPreRows = 128;  // query rows per workgroup
+constexpr int kPartRow = 132;  // floats per row of a split partial: m, l, two unused, O[128] (16-byte aligned)
 
 template <bool kAligned, bool kPow2>
 __global__ __launch_bounds__(kPreThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_mfma_kernel(
     const uint16_t* __restrict__ q, int64_t q_stride, const uint16_t* __restrict__ k_cache,
     const uint16_t* __restrict__ v_cache, const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k,
     const int32_t* __restrict__ block_table, int32_t mbps, int32_t batch, int32_t Hq, int32_t Hkv, int32_t bs,
-    int32_t bs_shift, float scale_log2, void* __restrict__ out, int out_bf16, int32_t n_qtiles, int32_t n_work) {
-  // ---- which (KV head, sequence, query tile, query head) this workgroup computes
+    int32_t bs_shift, float scale_log2, void* __restrict__ out, int out_bf16, int32_t n_qtiles, int32_t n_work,
+    int32_t n_splits, float* __restrict__ part) {
+  // ---- which (KV head, sequence, query tile, key split, query head) this workgroup computes
   const int per_xcd = (int(gridDim.x) + 7) >> 3;
   const int logical = int(blockIdx.x & 7) * per_xcd + int(blockIdx.x >> 3);
   if (logical >= n_work) return;
   const int G = Hq / Hkv;
   const int gi = logical % G;
   int rest = logical / G;
+  const int sp = rest % n_splits;
+  rest /= n_splits;
   const int s = rest % batch;
   rest /= batch;
   const int qtile = n_qtiles - 1 - rest % n_qtiles;
@@ -57,7 +62,25 @@ __global__ __launch_bounds__(kPreThreads) __attribute__((amdgpu_waves_per_eu(2, 
   const int past = k_len - q_len;  // position of row 0
   const int row_end = min(q_len, row0 + kPreRows);
   const int n_keys = past + row_end;  // keys needed by the last row of the tile
-  const int n_tiles = (n_keys + kPreKeys - 1) / kPreKeys;
+  const int n_tiles_all = (n_keys + kPreKeys - 1) / kPreKeys;
+  // Split sp of n_splits takes key tiles [t0, t1) of the workgroup's tiles (all of them when n_splits == 1); its
+  // loads stop at key t1 * 64, and its rows leave unnormalised partials for the merge pass.
+  const int per_split = (n_tiles_all + n_splits - 1) / n_splits;
+  const int t0 = sp * per_split;
+  const int t1 = min(n_tiles_all, t0 + per_split);
+  const int n_tiles = t1 - t0;
+  const int k_lim = min(k_len, t1 * kPreKeys);
+  // first row of this workgroup's partials (split mode only): [item][split][row][kPartRow]
+  const int64_t prow0 =
+      ((int64_t((int64_t(s) * n_qtiles + qtile) * Hq + (kvh * G + gi)) * n_splits + sp) * kPreRows) * kPartRow;
+  if (n_tiles <= 0) {  // an empty split (only when n_splits > 1): its rows' partials say "no keys"
+    const int r = int(threadIdx.x);
+    if (r < kPreRows && row0 + r < q_len) {
+      part[prow0 + int64_t(r) * kPartRow] = -INFINITY;
+      part[prow0 + int64_t(r) * kPartRow + 1] = 0.f;
+    }
+    return;
+  }
 
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -104,12 +127,14 @@ __global__ __launch_bounds__(kPreThreads) __attribute__((amdgpu_waves_per_eu(2, 
   const int va_off = (4 * (g4 >> 1) + (li >> 2)) * kVRow + 16 * (g4 & 1) + 4 * (li & 3);
 
   u32x4 kst[kPieces], vst[kPieces];
-  // prologue: K tiles 0 and 1, V tile 0 in LDS (their loads issued together: one round trip); scores of tile 0
+  // prologue: K tiles t0 and t0+1, V tile t0 in LDS (their loads issued together: one round trip); scores of
+  // tile t0
   {
     u32x4 k1st[kPieces];
-    pf_gload1<kAligned, kPow2>(kst, kbase, table, 0, k_len, bs, bs_shift, row_bytes, tid);
-    pf_gload1<kAligned, kPow2>(vst, vbase, table, 0, k_len, bs, bs_shift, row_bytes, tid);
-    pf_gload1<kAligned, kPow2>(k1st, kbase, table, kPreKeys, k_len, bs, bs_shift, row_bytes, tid);
+    const int kb0 = t0 * kPreKeys;
+    pf_gload1<kAligned, kPow2>(kst, kbase, table, kb0, k_lim, bs, bs_shift, row_bytes, tid);
+    pf_gload1<kAligned, kPow2>(vst, vbase, table, kb0, k_lim, bs, bs_shift, row_bytes, tid);
+    pf_gload1<kAligned, kPow2>(k1st, kbase, table, kb0 + kPreKeys, k_lim, bs, bs_shift, row_bytes, tid);
     pf_lstore_k(kst, kt[0], tid);
     pf_lstore_v(vst, vt[0], tid);
     pf_lstore_k(k1st, kt[1], tid);
@@ -117,14 +142,14 @@ __global__ __launch_bounds__(kPreThreads) __attribute__((amdgpu_waves_per_eu(2, 
   __syncthreads();
   f32x16 sa[kSub], sb[kSub];
   pf_scores(sa, kt[0], ka_off, qb);
-  __syncthreads();  // K tile 0 has been read by every wave before iteration 0 replaces it
+  __syncthreads();  // K tile t0 has been read by every wave before the first step replaces it
 
   auto step = [&](int j, f32x16 (&cur)[kSub], f32x16 (&nxt)[kSub], auto par) {
-    constexpr int P = decltype(par)::value;  // j % 2
+    constexpr int P = decltype(par)::value;  // (j - t0) % 2
     const int kb = j * kPreKeys;
-    // K tile j+2 and V tile j+1 start loading (past the end they read as zero and touch no memory)
-    pf_gload1<kAligned, kPow2>(kst, kbase, table, kb + 2 * kPreKeys, k_len, bs, bs_shift, row_bytes, tid);
-    pf_gload1<kAligned, kPow2>(vst, vbase, table, kb + kPreKeys, k_len, bs, bs_shift, row_bytes, tid);
+    // K tile j+2 and V tile j+1 start loading (past the split's end they read as zero and touch no memory)
+    pf_gload1<kAligned, kPow2>(kst, kbase, table, kb + 2 * kPreKeys, k_lim, bs, bs_shift, row_bytes, tid);
+    pf_gload1<kAligned, kPow2>(vst, vbase, table, kb + kPreKeys, k_lim, bs, bs_shift, row_bytes, tid);
     if (j < wave_tiles) {
       if (kb + kPreKeys - 1 > past + wave_row0) pf_mask(cur, my_pos - kb - 4 * hh);
       const float mh = pf_halfmax(cur) * scale_log2;
@@ -144,7 +169,9 @@ __global__ __launch_bounds__(kPreThreads) __attribute__((amdgpu_waves_per_eu(2, 
         m = mn;
         started = true;
       }
-      pf_weights_pv(cur, o, m, lsum, vt[P], va_off, scale_log2);
+      // a row that has seen no key yet (possible in a split that starts after its position) keeps m = -inf and
+      // all its scores are -inf: its weights are formed against 0, so they are 0 and not NaN
+      pf_weights_pv(cur, o, m == -INFINITY ? 0.f : m, lsum, vt[P], va_off, scale_log2);
       pf_lstore_k(kst, kt[P], tid);      // K tile j+2 replaces K tile j (scored in the previous step)
       pf_lstore_v(vst, vt[1 - P], tid);  // V tile j+1 replaces V tile j-1 (read by the previous step's PV)
     } else {
@@ -153,13 +180,27 @@ __global__ __launch_bounds__(kPreThreads) __attribute__((amdgpu_waves_per_eu(2, 
     }
     __syncthreads();
   };
-  for (int j = 0; j < n_tiles; j += 2) {
-    step(j, sa, sb, std::integral_constant<int, 0>());
-    if (j + 1 < n_tiles) step(j + 1, sb, sa, std::integral_constant<int, 1>());
+  for (int jr = 0; jr < n_tiles; jr += 2) {
+    step(t0 + jr, sa, sb, std::integral_constant<int, 0>());
+    if (jr + 1 < n_tiles) step(t0 + jr + 1, sb, sa, std::integral_constant<int, 1>());
   }
 
   if (my_row >= q_len) return;
   lsum = xhalf_sum(lsum);
+  if (n_splits > 1) {  // unnormalised partial: m (scaled log2 units), l, O; the merge pass finishes the row
+    float* pr = part + prow0 + int64_t(my_row - row0) * kPartRow;
+    if (hh == 0) {
+      pr[0] = m;
+      pr[1] = lsum;
+    }
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        *reinterpret_cast<f32x4*>(pr + 4 + 32 * mt + 8 * j + 4 * hh) =
+            f32x4{o[mt][4 * j], o[mt][4 * j + 1], o[mt][4 * j + 2], o[mt][4 * j + 3]};
+    return;
+  }
   const float inv = 1.f / lsum;
   // o[mt][i] is O^T[d = 32mt + 8(i/4) + 4hh + (i%4)][query column lr]
   const int64_t ob = (int64_t(q0 + my_row) * Hq + h) * 128 + 4 * hh;
@@ -181,12 +222,80 @@ __global__ __launch_bounds__(kPreThreads) __attribute__((amdgpu_waves_per_eu(2, 
   }
 }
 
+// Key splits of a call (host sizes only): when the grid holds fewer workgroups than the chip runs at once (two per
+// CU on the 256 CUs), each workgroup's key tiles are split so that about that many run, each split at least
+// kMinSplitKeys keys, at most kMaxSplits splits. One split leaves the output to the attention kernel itself.
+constexpr int64_t kPrefillSlots = 512;
+constexpr int64_t kMinSplitKeys = 1024;
+constexpr int64_t kMaxSplits = 32;
+
+int32_t prefill_splits(int32_t batch, int32_t max_seqlen_q, int32_t max_seqlen_k, int32_t Hq) {
+  const int64_t n_qtiles = (int64_t(max_seqlen_q) + kPreRows - 1) / kPreRows;
+  const int64_t n_work = int64_t(batch) * n_qtiles * Hq;
+  if (n_work <= 0 || n_work >= kPrefillSlots) return 1;
+  int64_t sp = (kPrefillSlots + n_work - 1) / n_work;
+  sp = std::min(sp, int64_t(max_seqlen_k) / kMinSplitKeys);
+  sp = std::min(sp, kMaxSplits);
+  return int32_t(std::max<int64_t>(sp, 1));
+}
+
+size_t prefill_mfma_workspace_bytes(int32_t batch, int32_t max_seqlen_q, int32_t max_seqlen_k, int32_t Hq) {
+  const int32_t sp = prefill_splits(batch, max_seqlen_q, max_seqlen_k, Hq);
+  if (sp <= 1) return 0;
+  const int64_t n_qtiles = (int64_t(max_seqlen_q) + kPreRows - 1) / kPreRows;
+  return size_t(int64_t(batch) * n_qtiles * Hq * sp * kPreRows * kPartRow) * sizeof(float);
+}
+
+// Merge of a row's split partials: M = max m_i, L = sum l_i 2^(m_i - M), O = sum O_i 2^(m_i - M) / L (splits with
+// no key for the row have m = -inf and weight 0). One wave per (token, query head), two of the 128 d per lane.
+__global__ __launch_bounds__(64) void prefill_merge_kernel(const int32_t* __restrict__ cu_q, int32_t batch, int32_t Hq,
+                                                           int32_t n_qtiles, int32_t n_splits,
+                                                           const float* __restrict__ part, void* __restrict__ out,
+                                                           int out_bf16) {
+  const int t = blockIdx.x;
+  const int h = blockIdx.y;
+  const int lane = threadIdx.x;
+  int a = 0, b = batch;  // the sequence of token t: cu_q[a] <= t < cu_q[a + 1]
+  while (b - a > 1) {
+    const int mid = (a + b) >> 1;
+    if (cu_q[mid] <= t) a = mid; else b = mid;
+  }
+  const int r = t - cu_q[a];
+  const int qtile = r / kPreRows;
+  const int row = r - qtile * kPreRows;
+  const int64_t sstride = int64_t(kPreRows) * kPartRow;
+  const float* p = part + ((int64_t((int64_t(a) * n_qtiles + qtile) * Hq + h) * n_splits) * kPreRows + row) * kPartRow;
+  const float mj = lane < n_splits ? p[lane * sstride] : -INFINITY;
+  const float lj = lane < n_splits ? p[lane * sstride + 1] : 0.f;
+  const float M = wave_max(mj);  // split 0 holds key 0, which every row sees: M is finite
+  const float wj = mj == -INFINITY ? 0.f : exp2f(mj - M);
+  const float L = wave_sum(wj * lj);
+  float a0 = 0.f, a1 = 0.f;
+  for (int j = 0; j < n_splits; ++j) {
+    const float w = __shfl(wj, j, 64);
+    if (w != 0.f) {  // wave-uniform; a split without keys for the row left no O
+      const float2 v = *reinterpret_cast<const float2*>(p + j * sstride + 4 + 2 * lane);
+      a0 += w * v.x;
+      a1 += w * v.y;
+    }
+  }
+  const float inv = 1.f / L;
+  const int64_t ob = (int64_t(t) * Hq + h) * 128 + 2 * lane;
+  if (out_bf16) {
+    *reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(out) + ob) = pack_bf16x2(a0 * inv, a1 * inv);
+  } else {
+    *reinterpret_cast<float2*>(static_cast<float*>(out) + ob) = make_float2(a0 * inv, a1 * inv);
+  }
+}
+
 void launch_prefill_mfma(const void* q, int64_t q_stride, const void* k_cache, const void* v_cache,
                          const int32_t* cu_q, const int32_t* cu_k, const int32_t* block_table, int32_t mbps,
-                         int32_t batch, int32_t max_seqlen_q, int32_t Hq, int32_t Hkv, int32_t block_size,
-                         float scale, void* out, bool out_bf16, hipStream_t stream) {
+                         int32_t batch, int32_t total_q, int32_t max_seqlen_q, int32_t max_seqlen_k, int32_t Hq,
+                         int32_t Hkv, int32_t block_size, float scale, void* out, bool out_bf16, void* workspace,
+                         hipStream_t stream) {
   const int n_qtiles = (max_seqlen_q + kPreRows - 1) / kPreRows;
-  const int n_work = batch * n_qtiles * Hq;
+  const int n_splits = prefill_splits(batch, max_seqlen_q, max_seqlen_k, Hq);
+  const int n_work = batch * n_qtiles * Hq * n_splits;
   const int grid = ((n_work + 7) / 8) * 8;
   const float sl2 = scale * kLog2e;
   const bool pow2 = (block_size & (block_size - 1)) == 0;
@@ -196,15 +305,19 @@ void launch_prefill_mfma(const void* q, int64_t q_stride, const void* k_cache, c
   const uint16_t* qp = static_cast<const uint16_t*>(q);
   const uint16_t* kc = static_cast<const uint16_t*>(k_cache);
   const uint16_t* vc = static_cast<const uint16_t*>(v_cache);
+  float* part = static_cast<float*>(workspace);
 #define PA_LAUNCH_PF(A, P)                                                                                      \
   hipLaunchKernelGGL((prefill_mfma_kernel<A, P>), dim3(grid), dim3(kPreThreads), 0, stream, qp, q_stride, kc, vc, \
                      cu_q, cu_k, block_table, mbps, batch, Hq, Hkv, block_size, shift, sl2, out, int(out_bf16),  \
-                     n_qtiles, n_work)
+                     n_qtiles, n_work, n_splits, part)
   if (aligned && pow2) PA_LAUNCH_PF(true, true);
   else if (aligned) PA_LAUNCH_PF(true, false);
   else if (pow2) PA_LAUNCH_PF(false, true);
   else PA_LAUNCH_PF(false, false);
 #undef PA_LAUNCH_PF
+  if (n_splits > 1)
+    hipLaunchKernelGGL(prefill_merge_kernel, dim3(unsigned(total_q), unsigned(Hq)), dim3(64), 0, stream, cu_q, batch,
+                       Hq, n_qtiles, n_splits, part, out, int(out_bf16));
 }
 
 }  // namespace pa

@@ -201,6 +201,20 @@ def test_decode_workspace_query():
         pa.decode_workspace_bytes(4, 32, 1, 128, 128, 256, pa.decode_split_tokens(4, 32, 1, 128, 128, 256))
 
 
+def test_prefill_workspace_query():
+    # enough workgroups (or head_dim other than 128, or short keys): one split, no workspace
+    assert pa.prefill_workspace_bytes(1, 32, 128, 2048, 32768) == 0      # 16 query tiles x 32 heads = 512
+    assert pa.prefill_workspace_bytes(8, 32, 128, 1544, 1798) == 0
+    assert pa.prefill_workspace_bytes(1, 32, 64, 200, 8392) == 0
+    assert pa.prefill_workspace_bytes(2, 8, 128, 200, 600) == 0         # under 1024 keys
+    # 2 query tiles x 32 heads = 64 workgroups: 8 splits of partial rows m, l, 2 unused, O[128] (132 floats)
+    assert pa.prefill_workspace_bytes(1, 32, 128, 200, 8392) == 1 * 2 * 32 * 8 * 128 * 132 * 4
+    # one row over 5001 keys: 32 workgroups, splits limited to one per 1024 keys
+    assert pa.prefill_workspace_bytes(1, 32, 128, 1, 5001) == 1 * 1 * 32 * 4 * 128 * 132 * 4
+    # at most 32 splits
+    assert pa.prefill_workspace_bytes(1, 1, 128, 1, 10 ** 6) == 32 * 128 * 132 * 4
+
+
 def test_binding_checks_layouts_on_the_host():
     import torch
 

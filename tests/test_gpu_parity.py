@@ -62,6 +62,13 @@ def test_chunked_qwen3_8b_config_sampled_rows():
     _run_and_check(wl, seqs=[0], rows=rows)
 
 
+def test_chunk256_qwen3_8b_sampled_rows():
+    """256 new rows over 32512 cached keys (eight key splits per workgroup and the merge pass)."""
+    wl = make_config("chunk256_qwen3_8b")
+    rows = {0: np.concatenate([np.arange(0, 40), np.arange(120, 136), np.arange(216, 256)])}
+    _run_and_check(wl, seqs=[0], rows=rows)
+
+
 @pytest.fixture(scope="module")
 def decode_32b():
     return make_config("decode_qwen3_32b")
@@ -175,6 +182,31 @@ def test_decode_small(case):
     wl = build_decode(f"decode_small_{case}", 300 + case, Hq, Hkv, D, bs, dt, ctx,
                       num_blocks=sum(-(-n // bs) for n in ctx) + 2)
     _run_and_check(wl, split_tokens=split)
+
+
+# few query tiles over long keys: the prefill kernel splits each workgroup's key tiles (fewer workgroups than the
+# chip runs at once) and a merge pass combines the splits' partials. Chunks of 200 rows and of one row over
+# thousands of cached keys; a mixed batch where some rows see no key in a split (their split partial is empty);
+# 16-key blocks (tiles gathered key by key); sequences without new tokens
+PREFILL_SPLIT_CASES = [
+    # Hq, Hkv, D, bs, dtype, k_lens, cached, out_dtype
+    (32, 8, 128, 256, "bf16", [8392], [8192], "f32"),
+    (32, 8, 128, 256, "bf16", [5001], [5000], "f32"),
+    (8, 2, 128, 256, "bf16", [3000, 4100, 1500], [2900, 3800, 0], "f32"),
+    (16, 4, 128, 16, "bf16", [2100], [2000], "bf16"),
+    (16, 8, 128, 256, "bf16", [5005, 9000, 70], [5000, 9000, 0], "f32"),
+]
+
+
+@pytest.mark.parametrize("case", range(len(PREFILL_SPLIT_CASES)))
+def test_prefill_key_splits(case):
+    Hq, Hkv, D, bs, dt, kl, cached, odt = PREFILL_SPLIT_CASES[case]
+    q_lens = [k - c for k, c in zip(kl, cached)]
+    need = pa.prefill_workspace_bytes(len(kl), Hq, D, max(q_lens), max(kl))
+    assert need > 0, "the case must take the split path"
+    wl = build_prefill(f"prefill_split_{case}", 700 + case, Hq, Hkv, D, bs, dt, kl, cached,
+                       num_blocks=sum(-(-n // bs) for n in kl) + 3, allow_empty=0 in q_lens)
+    _run_and_check(wl, out_dtype=torch.bfloat16 if odt == "bf16" else torch.float32)
 
 
 @pytest.mark.parametrize("bs", [16, 256])

@@ -350,12 +350,20 @@ def _chunked_8b(seed: int = 105, fill: bool = True) -> Workload:
                          outlier_p=0.01, table_width=128, fill=fill)
 
 
+def _chunk256_8b(seed: int = 106, fill: bool = True) -> Workload:
+    """A small chunk over a long prefix (chunked prefill at its smallest useful size): the chunked recipe with
+    256 new rows after 32512 cached keys, so one sequence has 2 query tiles per head."""
+    return build_prefill("chunk256_qwen3_8b", seed, 32, 8, 128, 256, "bf16", [32768], [32512], num_blocks=128,
+                         outlier_p=0.01, table_width=128, fill=fill)
+
+
 _BUILDERS = {
     "tiny": _tiny,
     "decode_qwen3_0p6b": _decode_0p6b,
     "prefill_qwen3_8b": _prefill_8b,
     "decode_qwen3_32b": _decode_32b,
     "chunked_qwen3_8b": _chunked_8b,
+    "chunk256_qwen3_8b": _chunk256_8b,
 }
 
 
@@ -386,11 +394,11 @@ def build_rope_inputs(seed: int, num_tokens: int, num_heads: int, num_kv_heads: 
 
 
 _SEEDS = {"tiny": 101, "decode_qwen3_0p6b": 102, "prefill_qwen3_8b": 103, "decode_qwen3_32b": 104,
-          "chunked_qwen3_8b": 105}
+          "chunked_qwen3_8b": 105, "chunk256_qwen3_8b": 106}
 
 
 def make_config(name: str, seed: int | None = None, fill: bool = True) -> Workload:
-    """The named workload with its fixed seed (101..105), or another seed of the same recipe.
+    """The named workload with its fixed seed (101..106), or another seed of the same recipe.
 
     fill=False skips drawing the pool (k_cache/v_cache are None); lengths, tables and Q/K/V are still drawn.
     """
