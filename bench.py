@@ -79,7 +79,9 @@ def algorithmic_work(wl, step, out_bytes: int):
 # summary taken on other sources is stale and not reported.
 ATTN_SOURCES = {"decode": ("pa_decode_stream.hip", "pa_decode_tile.h", "pa_common.h", "pa_api.hip"),
                 "prefill": ("pa_prefill.hip", "pa_prefill_tile.h", "pa_common.h", "pa_api.hip")}
-ATTN_KERNELS = {"decode": ("decode_stream_kernel", "decode_stream_merge_kernel"), "prefill": ("prefill_mfma_kernel",)}
+ATTN_KERNELS = {"decode": ("decode_stream_kernel", "decode_stream_merge_kernel"),
+                "prefill": ("prefill_mfma_kernel", "prefill_merge_kernel")}
+ATTN_KERNELS_OPTIONAL = {"prefill_merge_kernel"}  # launched only by calls that split their keys
 
 
 def _code_text(src: str) -> str:
@@ -144,6 +146,8 @@ def write_traffic_summary(workload: str, fetch_csv: str, write_csv: str) -> dict
     fscale, wscale = known_kib / copy_f, known_kib / copy_w
     per, total = {}, 0.0
     for kn in ATTN_KERNELS[kind]:
+        if kn in ATTN_KERNELS_OPTIONAL and not any(kn in k for k in fetch):
+            continue
         fk, n = mean(fetch, kn)
         wk, _ = mean(write, kn)
         b = (fk * fscale + wk * wscale) * 1024
