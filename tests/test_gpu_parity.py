@@ -351,10 +351,13 @@ def _relabel(wl, perm):
     return kc, vc, type(st)(st.kind, bt, st.num_cached, st.num_new, st.q, st.k, st.v)
 
 
-@pytest.mark.parametrize("kind", ["prefill", "decode"])
+@pytest.mark.parametrize("kind", ["prefill", "prefill_split", "decode"])
 def test_physical_relabelling_is_bit_identical(kind):
     if kind == "prefill":
         wl = build_prefill("perm_p", 500, 32, 8, 128, 64, "bf16", [300, 129, 500], [64, 0, 128], num_blocks=20)
+    elif kind == "prefill_split":  # key splits + merge (one 100-row chunk over 4000 keys)
+        wl = build_prefill("perm_ps", 502, 32, 8, 128, 64, "bf16", [4100], [4000], num_blocks=70)
+        assert pa.prefill_workspace_bytes(1, 32, 128, 100, 4100) > 0
     else:
         wl = build_decode("perm_d", 501, 64, 8, 128, 64, "bf16", [300, 129, 1500], num_blocks=40)
     perm = np.random.default_rng(3).permutation(wl.num_blocks)
@@ -367,10 +370,13 @@ def test_physical_relabelling_is_bit_identical(kind):
     assert torch.equal(outs[0], outs[1])
 
 
-@pytest.mark.parametrize("kind", ["prefill", "decode"])
+@pytest.mark.parametrize("kind", ["prefill", "prefill_split", "decode"])
 def test_nan_in_unreferenced_slots_does_not_reach_output(kind):
     if kind == "prefill":
         wl = build_prefill("nan_p", 510, 32, 8, 128, 256, "bf16", [300, 77], [256, 0], num_blocks=6)
+    elif kind == "prefill_split":  # the key ranges of the splits end inside blocks whose tails hold NaN
+        wl = build_prefill("nan_ps", 512, 32, 8, 128, 256, "bf16", [3000, 77], [2950, 0], num_blocks=16)
+        assert pa.prefill_workspace_bytes(2, 32, 128, 77, 3000) > 0
     else:
         wl = build_decode("nan_d", 511, 16, 8, 128, 256, "bf16", [300, 77, 513], num_blocks=8)
     st = wl.steps[0]
