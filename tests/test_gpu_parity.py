@@ -139,6 +139,8 @@ PREFILL_CASES = [
     (16, 8, 128, 64, "bf16", [500, 64, 65, 1], [436, 0, 1, 0]),
     # block size 1 (every key its own block)
     (8, 2, 128, 1, "bf16", [17, 5], [3, 0]),
+    # 512-key blocks; 16 query heads per KV head
+    (16, 1, 128, 512, "bf16", [1100, 513, 40], [512, 0, 39]),
 ]
 
 
@@ -170,6 +172,9 @@ DECODE_CASES = [
     (8, 2, 128, 96, "bf16", [1, 96, 97, 500, 192, 191], 0),
     # 3 KV heads: the balanced decode's groups of Hkv workers do not divide its worker count
     (12, 3, 128, 64, "bf16", [5, 700, 64, 65, 1000, 3000], 0),
+    # 64 KV heads, one query head each (groups of 64 workers); 512-key blocks
+    (64, 64, 128, 32, "bf16", [100, 3000, 33], 0),
+    (16, 8, 128, 512, "bf16", [1, 511, 512, 513, 2600], 0),
     # block size 1; 32 query heads per KV head (beyond the MFMA kernels' 16: the generic kernel)
     (8, 2, 128, 1, "bf16", [17, 1, 40], 0),
     (32, 1, 128, 16, "bf16", [50, 300], 0),
@@ -228,7 +233,7 @@ def test_decode_largest_batch():
 # the decode step with the new K/V given (pa_decode_append: store inside the balanced decode's pass) on every
 # decode shape it takes: 1..20000 keys, block sizes 32 to 256 (96 among them), G = 2 to 16, 300 and 4096
 # sequences, the Qwen3-0.6B workload's steps; the caches must match the oracle's bit for bit after each step
-APPEND_CASES = [0, 8, 9, 10, 11, 12]
+APPEND_CASES = [0, 8, 9, 10, 11, 12, 13, 14]
 
 
 @pytest.mark.parametrize("case", APPEND_CASES)
@@ -247,7 +252,7 @@ def test_decode_append_qwen3_0p6b_config_and_largest_batch():
     _run_and_check(wl, append=True, out_dtype=torch.bfloat16)
 
 
-@pytest.mark.parametrize("case", [3, 6, 14])
+@pytest.mark.parametrize("case", [3, 6, 16])
 def test_decode_append_falls_back_on_other_shapes(case):
     """Block size 16, float32, 32 query heads per KV head: the binding stores and decodes in separate calls."""
     Hq, Hkv, D, bs, dt, ctx, _ = DECODE_CASES[case]
@@ -270,7 +275,7 @@ def test_decode_append_falls_back_on_other_shapes(case):
 # metadata and store in one launch (pa_build_metadata_store) on shapes of the cases above: bf16 and f32 rows of
 # 64 to 4096 bytes, block sizes 1 to 256, sequences without new tokens, 300 and 4096 sequences
 FUSED_STORE_CASES = [("prefill", 0), ("prefill", 4), ("prefill", 5), ("prefill", 6), ("prefill", 10),
-                     ("decode", 0), ("decode", 9), ("decode", 11), ("decode", 13)]
+                     ("decode", 0), ("decode", 9), ("decode", 11), ("decode", 15)]
 
 
 @pytest.mark.parametrize("case", FUSED_STORE_CASES)
