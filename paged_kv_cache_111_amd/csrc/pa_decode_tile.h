@@ -75,11 +75,12 @@ __device__ __forceinline__ void load_tile(KVTile& t, const char* __restrict__ kb
     for (int tt = 0; tt < 2; ++tt) {
       const int off = int(lo.k) + int(16 * tt * row_bytes);
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) t.k[tt][ks] = __builtin_amdgcn_raw_buffer_load_b128(kr, off + 64 * ks, 0, 0);
+      for (int ks = 0; ks < 4; ++ks)
+        t.k[tt][ks] = __builtin_amdgcn_raw_buffer_load_b128(kr, off + 64 * ks, 0, kLoadStream);
     }
 #pragma unroll
     for (int it = 0; it < 8; ++it)
-      t.v[it] = __builtin_amdgcn_raw_buffer_load_b128(vr, int(lo.v) + int(4 * it * row_bytes), 0, 0);
+      t.v[it] = __builtin_amdgcn_raw_buffer_load_b128(vr, int(lo.v) + int(4 * it * row_bytes), 0, kLoadStream);
   } else {
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
@@ -87,7 +88,7 @@ __device__ __forceinline__ void load_tile(KVTile& t, const char* __restrict__ kb
       if (key < t1) {
         const char* kp = kbase + slot_of_key<kPow2>(table, key, bs, bs_shift) * row_bytes + 16 * lg;
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) t.k[tt][ks] = ld16(kp + 64 * ks);
+        for (int ks = 0; ks < 4; ++ks) t.k[tt][ks] = ld16_stream(kp + 64 * ks);
       } else {
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) t.k[tt][ks] = z;
@@ -96,7 +97,7 @@ __device__ __forceinline__ void load_tile(KVTile& t, const char* __restrict__ kb
 #pragma unroll
     for (int it = 0; it < 8; ++it) {
       const int key = base + 4 * it + lg;
-      t.v[it] = key < t1 ? ld16(vbase + slot_of_key<kPow2>(table, key, bs, bs_shift) * row_bytes + 16 * li) : z;
+      t.v[it] = key < t1 ? ld16_stream(vbase + slot_of_key<kPow2>(table, key, bs, bs_shift) * row_bytes + 16 * li) : z;
     }
   }
 }
