@@ -40,8 +40,10 @@ __device__ __forceinline__ int64_t stream_chunk(int64_t total, int32_t n_workers
   return max(((total + n_workers - 1) / n_workers + 31) & ~int64_t(31), kMinChunk);
 }
 
+// Tiles whose loads are in flight per worker. With the non-temporal policy on the K/V loads one tile ahead
+// measured 1% faster than two on the 0.6B mix (the same on long contexts), in 173 registers instead of 247.
 #ifndef PA_STREAM_NBUF
-#define PA_STREAM_NBUF 2
+#define PA_STREAM_NBUF 1
 #endif
 constexpr int kStreamNBuf = PA_STREAM_NBUF;
 
