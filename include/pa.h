@@ -219,7 +219,8 @@ pa_status pa_prefill_varlen(const void* q, int64_t q_tok_stride, const void* k_c
                             void* out, pa_dtype out_dtype, void* workspace, size_t workspace_bytes, void* stream);
 
 /* Workspace bytes pa_prefill_varlen needs for these host sizes: 0 unless the call splits its keys (then
- * batch * ceil(max_seqlen_q / 128) * num_heads * splits * 128 rows of 132 floats). */
+ * batch * ceil(max_seqlen_q / 128) * num_heads * splits * 128 rows of 132 floats). The query sees no dtype: for
+ * head_dim 128 it answers for the bf16 kernel, and an fp32 call of the same sizes leaves the workspace unused. */
 size_t pa_prefill_workspace_bytes(int32_t batch, int32_t num_heads, int32_t head_dim, int32_t max_seqlen_q,
                                   int32_t max_seqlen_k);
 
