@@ -195,3 +195,50 @@ def test_graph_decode_append_replays(batch):
         assert torch.isfinite(out_e).all(), f"replay {r}: eager output not finite"
         assert torch.equal(out_g, out_e), f"replay {r}: graph output differs from store + decode"
         assert torch.equal(kc_g, kc_e) and torch.equal(vc_g, vc_e), f"replay {r}: caches differ"
+
+
+@pytest.mark.gpu
+def test_two_streams_at_once_match_sequential_calls():
+    """The library keeps no per-call state of its own: decode steps enqueued on two streams at the same time
+    (separate caches, outputs and workspaces) give the results of the same calls made one after the other."""
+    rng = np.random.default_rng(990)
+    B, mbps = 32, 8
+    nb = B * mbps + 4
+
+    def setup():
+        table = rng.permutation(nb).astype(np.int32)[: B * mbps].reshape(B, mbps)
+        kc = _bf16(rng, (nb, BS, HKV, D)).to(DEV)
+        vc = _bf16(rng, (nb, BS, HKV, D)).to(DEV)
+        q = _bf16(rng, (B, HQ, D)).to(DEV)
+        kn = _bf16(rng, (B, HKV, D)).to(DEV)
+        vn = _bf16(rng, (B, HKV, D)).to(DEV)
+        cached = torch.from_numpy(rng.integers(0, mbps * BS, size=B).astype(np.int32)).to(DEV)
+        return dict(table=torch.from_numpy(table).to(DEV), kc=kc, vc=vc, q=q, kn=kn, vn=vn, cached=cached)
+
+    jobs = [setup(), setup()]
+    need = pa.decode_workspace_bytes(B, HQ, HKV, D, mbps, BS, 0)
+    scale = 1.0 / np.sqrt(D)
+
+    def run(j, out, ws, kc, vc, stream=None):
+        pa.decode_append(j["q"], j["kn"], j["vn"], kc, vc, j["cached"], j["table"], scale, out=out, workspace=ws,
+                         fallback=False, stream=stream)
+
+    # sequential reference on copies of the caches
+    ref = []
+    for j in jobs:
+        out = torch.empty((B, HQ, D), dtype=torch.float32, device=DEV)
+        kc, vc = j["kc"].clone(), j["vc"].clone()
+        run(j, out, torch.empty(need, dtype=torch.uint8, device=DEV), kc, vc)
+        torch.cuda.synchronize()
+        ref.append((out, kc, vc))
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    outs = [torch.empty((B, HQ, D), dtype=torch.float32, device=DEV) for _ in jobs]
+    wss = [torch.empty(need, dtype=torch.uint8, device=DEV) for _ in jobs]
+    torch.cuda.synchronize()
+    for _ in range(3):  # repeated: the appended rows are stored again with the same values
+        for j, out, ws, st in zip(jobs, outs, wss, streams):
+            run(j, out, ws, j["kc"], j["vc"], stream=st)
+        torch.cuda.synchronize()
+        for (o_ref, kc_ref, vc_ref), out, j in zip(ref, outs, jobs):
+            assert torch.equal(out, o_ref)
+            assert torch.equal(j["kc"], kc_ref) and torch.equal(j["vc"], vc_ref)

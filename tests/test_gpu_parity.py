@@ -223,6 +223,32 @@ def test_prefill_with_sequences_without_new_tokens(bs):
     _run_and_check(wl)
 
 
+def test_decode_batch_beyond_the_balanced_limit():
+    """5000 sequences (more than the 4096 whose prefix sums the balanced decode and the metadata build keep in
+    LDS): with slots and lengths from the host, pa_store_kvcache and pa_decode (its fixed-split kernels) match
+    the oracle; pa_decode_append refuses the batch before launching, as its fallback's metadata build does."""
+    ctx = [int(x) for x in np.random.default_rng(12).integers(1, 90, 5000)]
+    wl = build_decode("decode_5000", 621, 8, 2, 128, 32, "bf16", ctx, num_blocks=sum(-(-n // 32) for n in ctx) + 2)
+    step = wl.steps[0]
+    kc_h, vc_h = wl.k_cache.copy(), wl.v_cache.copy()
+    kc, vc = to_dev(wl.k_cache, wl.dtype), to_dev(wl.v_cache, wl.dtype)
+    ds = DevStep(step, wl.dtype)
+    print("[case] decode_5000", flush=True)
+    meta_r, ref = oracle_step(wl, step, kc_h, vc_h)
+    pa.store_kvcache(ds.k, ds.v, kc, vc, i32(meta_r["slot_mapping"]))
+    out = pa.decode(ds.q, kc, vc, i32(meta_r["context_lens"]), ds.block_table, wl.scale)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_host_bits(kc), kc_h) and np.array_equal(to_host_bits(vc), vc_h)
+    assert_close(out, ref, what="decode 5000")
+    kc0 = kc.clone()
+    with pytest.raises(pa.PAError, match="UNSUPPORTED"):
+        pa.decode_append(ds.q, ds.k, ds.v, kc, vc, ds.num_cached, ds.block_table, wl.scale, fallback=False)
+    with pytest.raises(pa.PAError, match="SHAPE"):
+        pa.decode_append(ds.q, ds.k, ds.v, kc, vc, ds.num_cached, ds.block_table, wl.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(kc, kc0)
+
+
 def test_decode_largest_batch():
     """4096 sequences (the largest batch of the balanced decode's prefix sums) of 1..64 keys."""
     ctx = [int(x) for x in np.random.default_rng(11).integers(1, 65, 4096)]
