@@ -248,6 +248,12 @@ pa_status pa_prefill_varlen(const void* q, int64_t q_tok_stride, const void* k_c
   if (batch == 0 || total_q == 0) return PA_OK;
   if (max_seqlen_q <= 0 || max_blocks_per_seq <= 0 || int64_t(max_seqlen_k) > int64_t(max_blocks_per_seq) * block_size)
     return PA_ERR_SHAPE;
+  // grids: heads are a y dimension (at most 65535) of the per-(row, head) kernels, and the matrix-core kernel's
+  // flat grid of (sequence, query tile, head, key split) workgroups must fit an int
+  if (num_heads > 65535 ||
+      int64_t(batch) * ((int64_t(max_seqlen_q) + 127) / 128) * num_heads *
+              pa::prefill_splits(batch, max_seqlen_q, max_seqlen_k, num_heads) > (int64_t(1) << 30))
+    return PA_ERR_SHAPE;
   if (!q || !k_cache || !v_cache || !cu_seqlens_q || !cu_seqlens_k || !block_table || !out) return PA_ERR_NULL;
   if (workspace_bytes < pa_prefill_workspace_bytes(batch, num_heads, head_dim, max_seqlen_q, max_seqlen_k))
     return PA_ERR_WORKSPACE;
@@ -303,7 +309,7 @@ pa_status pa_decode(const void* q, int64_t q_tok_stride, const void* k_cache, co
   if (q_tok_stride < int64_t(num_heads) * head_dim) return PA_ERR_SHAPE;
   if (!(softmax_scale > 0.f) || softmax_scale > 3.0e38f) return PA_ERR_SHAPE;
   if (batch == 0) return PA_OK;
-  if (max_blocks_per_seq <= 0 || batch > 65535) return PA_ERR_SHAPE;
+  if (max_blocks_per_seq <= 0 || batch > 65535 || num_heads > 65535) return PA_ERR_SHAPE;
   if (!q || !k_cache || !v_cache || !context_lens || !block_table || !out) return PA_ERR_NULL;
   hipStream_t st = static_cast<hipStream_t>(stream);
   const bool out_bf16 = out_dtype == PA_BF16;

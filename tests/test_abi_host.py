@@ -134,6 +134,9 @@ def test_prefill_rejects_bad_arguments():
     assert _prefill(odt=9) == b.PA_ERR_UNSUPPORTED
     assert _prefill(qs=100) == b.PA_ERR_SHAPE          # token stride shorter than Hq*D
     assert _prefill(msk=8 * 256 + 1) == b.PA_ERR_SHAPE  # longer than the table can address
+    # grids that would not fit: more than 65535 heads, or 2^30 workgroups of (sequence, query tile, head)
+    assert _prefill(hq=65536 + 8, hkv=8, qs=(65536 + 8) * 128) == b.PA_ERR_SHAPE
+    assert _prefill(batch=4096, msq=2 ** 21, total_q=2 ** 21) == b.PA_ERR_SHAPE
 
 
 def _decode(**kw):
@@ -150,6 +153,7 @@ def test_decode_rejects_bad_arguments():
     assert _decode(hq=60) == b.PA_ERR_SHAPE
     assert _decode(dtype=5) == b.PA_ERR_UNSUPPORTED
     assert _decode(bs=-4) == b.PA_ERR_SHAPE
+    assert _decode(hq=65536, hkv=8, qs=65536 * 128) == b.PA_ERR_SHAPE
 
 
 def _append(**kw):
