@@ -242,3 +242,82 @@ def test_two_streams_at_once_match_sequential_calls():
         for (o_ref, kc_ref, vc_ref), out, j in zip(ref, outs, jobs):
             assert torch.equal(out, o_ref)
             assert torch.equal(j["kc"], kc_ref) and torch.equal(j["vc"], vc_ref)
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("kind", ["decode", "prefill_split"])
+def test_workspace_contents_do_not_matter(kind):
+    """The workspace is scratch: every partial a call reads back it wrote in the same call. A workspace full of
+    NaN bytes gives the bit-identical output of a zeroed one."""
+    rng = np.random.default_rng(995)
+    mbps = 40 if kind == "prefill_split" else 8
+    B = 1 if kind == "prefill_split" else 48
+    nb = B * mbps + 4
+    table = torch.from_numpy(rng.permutation(nb).astype(np.int32)[: B * mbps].reshape(B, mbps)).to(DEV)
+    kc = _bf16(rng, (nb, BS, HKV, D)).to(DEV)
+    vc = _bf16(rng, (nb, BS, HKV, D)).to(DEV)
+    scale = 1.0 / np.sqrt(D)
+    outs = []
+    for fill in (0x00, 0xFF):  # 0xFFFF... is a NaN in every float width
+        if kind == "decode":
+            lens = torch.from_numpy(np.random.default_rng(7).integers(1, mbps * BS + 1, size=B).astype(np.int32))
+            lens = lens.to(DEV)
+            q = _bf16(np.random.default_rng(8), (B, HQ, D)).to(DEV)
+            need = pa.decode_workspace_bytes(B, HQ, HKV, D, mbps, BS, 0)
+            ws = torch.full((need,), fill, dtype=torch.uint8, device=DEV)
+            outs.append(pa.decode(q, kc, vc, lens, table, scale, workspace=ws))
+        else:
+            q_len, k_len = 200, mbps * BS  # 200 rows over 10240 keys: key splits and the merge pass
+            q = _bf16(np.random.default_rng(9), (q_len, HQ, D)).to(DEV)
+            cu_q = torch.tensor([0, q_len], dtype=torch.int32, device=DEV)
+            cu_k = torch.tensor([0, k_len], dtype=torch.int32, device=DEV)
+            need = pa.prefill_workspace_bytes(1, HQ, D, q_len, k_len)
+            assert need > 0
+            ws = torch.full((need,), fill, dtype=torch.uint8, device=DEV)
+            outs.append(pa.prefill_varlen(q, kc, vc, cu_q, cu_k, table, q_len, k_len, scale, workspace=ws))
+        torch.cuda.synchronize()
+    assert torch.isfinite(outs[0]).all()
+    assert torch.equal(outs[0], outs[1])
+
+
+@pytest.mark.gpu
+def test_graph_prefill_with_key_splits_replays():
+    """The key-split prefill (split count and grids from host sizes only) captured once and replayed with new
+    queries and cache contents: every replay equals the eager call bit for bit."""
+    rng = np.random.default_rng(996)
+    mbps, q_len = 40, 200
+    k_len = mbps * BS
+    nb = mbps + 4
+    table = torch.from_numpy(rng.permutation(nb).astype(np.int32)[:mbps].reshape(1, mbps)).to(DEV)
+    kc = torch.empty((nb, BS, HKV, D), dtype=torch.bfloat16, device=DEV)
+    vc = torch.empty_like(kc)
+    q = torch.empty((q_len, HQ, D), dtype=torch.bfloat16, device=DEV)
+    cu_q = torch.tensor([0, q_len], dtype=torch.int32, device=DEV)
+    cu_k = torch.tensor([0, k_len], dtype=torch.int32, device=DEV)
+    need = pa.prefill_workspace_bytes(1, HQ, D, q_len, k_len)
+    ws_g = torch.empty(need, dtype=torch.uint8, device=DEV)
+    ws_e = torch.empty_like(ws_g)
+    out_g = torch.empty((q_len, HQ, D), dtype=torch.float32, device=DEV)
+    out_e = torch.empty_like(out_g)
+    scale = 1.0 / np.sqrt(D)
+
+    def draw():
+        kc.copy_(_bf16(rng, tuple(kc.shape)).to(DEV))
+        vc.copy_(_bf16(rng, tuple(vc.shape)).to(DEV))
+        q.copy_(_bf16(rng, tuple(q.shape)).to(DEV))
+        torch.cuda.synchronize()
+
+    draw()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        pa.prefill_varlen(q, kc, vc, cu_q, cu_k, table, q_len, k_len, scale, out=out_g, workspace=ws_g)
+    torch.cuda.synchronize()
+    for r in range(3):
+        if r > 0:
+            draw()
+        g.replay()
+        torch.cuda.synchronize()
+        pa.prefill_varlen(q, kc, vc, cu_q, cu_k, table, q_len, k_len, scale, out=out_e, workspace=ws_e)
+        torch.cuda.synchronize()
+        assert torch.isfinite(out_e).all()
+        assert torch.equal(out_g, out_e), f"replay {r}"
