@@ -286,6 +286,21 @@ class GpuWorkload:
             need = pa.prefill_workspace_bytes(st.batch, wl.num_heads, wl.head_dim, self.max_q, self.max_k)
         self.ws = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
 
+    def run_attention(self, layer: int):
+        """The attention call of the step alone (decode with append: the whole pa_decode_append call, whose store
+        rewrites the same rows; prefill and decode: the attention over the cache the step's store filled)."""
+        pa, wl, st = self.pa, self.wl, self.step
+        kc, vc = self.k_layers[layer], self.v_layers[layer]
+        if self.append:
+            pa.decode_append(self.q, self.k, self.v, kc, vc, self.num_cached, self.block_table, wl.scale,
+                             out=self.out, workspace=self.ws, fallback=False)
+        elif st.kind == "decode":
+            pa.decode(self.q, kc, vc, self.meta["context_lens"], self.block_table, wl.scale, out=self.out,
+                      workspace=self.ws)
+        else:
+            pa.prefill_varlen(self.q, kc, vc, self.meta["cu_seqlens_q"], self.meta["cu_seqlens_k"],
+                              self.block_table, self.max_q, self.max_k, wl.scale, out=self.out, workspace=self.ws)
+
     def run(self, layer: int, ev=None):
         """One step on layer `layer`'s pool; ev = (e0, e1, e2, e3) events around metadata, store, attention (with
         the fused launch, e0..e1 spans metadata and store, and e1..e2 is empty; with append, the decode call
@@ -316,6 +331,7 @@ class GpuWorkload:
             pa.store_kvcache(self.k, self.v, kc, vc, meta["slot_mapping"])
         if ev:
             ev[2].record()
+        self.meta = meta
         if st.kind == "decode":
             pa.decode(self.q, kc, vc, meta["context_lens"], self.block_table, wl.scale, out=self.out,
                       workspace=self.ws)
@@ -360,6 +376,16 @@ def time_workload(g: GpuWorkload, steps: int, warmup: int, n_layers: int):
         g.run(i % n_layers, evs[i])
     torch.cuda.synchronize()
     wall_ev = time.perf_counter() - t1
+    # third pass: the attention call alone, K calls back to back between one pair of events on the launch stream
+    # (no event between launches): the kernel time the roofline uses
+    e_a, e_b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e_a.record()
+    for i in range(steps):
+        g.run_attention(i % n_layers)
+    e_b.record()
+    torch.cuda.synchronize()
+    launch_ms = e_a.elapsed_time(e_b) / steps
     meta_ms = np.array([e[0].elapsed_time(e[1]) for e in evs])
     store_ms = np.array([e[1].elapsed_time(e[2]) for e in evs])
     attn_ms = np.array([e[2].elapsed_time(e[3]) for e in evs])
@@ -367,7 +393,13 @@ def time_workload(g: GpuWorkload, steps: int, warmup: int, n_layers: int):
     return {"wall_ms_per_step": 1e3 * wall / steps, "wall_ms_per_step_with_events": 1e3 * wall_ev / steps,
             "step_ms": float(np.mean(step_ms)), "meta_ms": float(np.mean(meta_ms)),
             "store_ms": float(np.mean(store_ms)), "attn_ms": float(np.mean(attn_ms)),
-            "attn_ms_median": float(np.median(attn_ms)), "attn_ms_min": float(np.min(attn_ms))}
+            "attn_ms_median": float(np.median(attn_ms)), "attn_ms_min": float(np.min(attn_ms)),
+            "launch_ms": launch_ms}
+
+
+# The batch sizes the engine captures its decode step for: 1, 2, 4, 8, then every multiple of 16 up to 512 (larger
+# batches run eagerly), "一个 prompt 的一生" §2.2.4 and §3.3.2.
+GRAPH_LADDER = [1, 2, 4, 8] + list(range(16, 513, 16))
 
 
 def graph_ladder(batches, iters: int = 200):
@@ -552,9 +584,11 @@ def sample_sweep(batches=(1, 64, 256), vocab: int = 151936, iters: int = 50):
 def cpu_baseline(wl, budget_s: float):
     """The oracle (as it stands) on the host: metadata, store and attention of the same step.
 
-    Whole passes over the batch are repeated until the time budget is spent; if one pass alone would exceed it,
-    the attention stops after the sequence that crosses the budget. The oracle's store writes the same rows on
-    every pass, so it runs in place on the workload's host pools.
+    Work units are whole sequences for decode and chunks of CPU_ROWS query rows of a sequence for prefill (a
+    single long chunk, like the 2048 rows over 32768 keys, would otherwise take tens of seconds). Units are
+    visited in the step's order, over repeated passes, until the time budget is spent; the rate counts the keys
+    (decode) or unmasked (query, key) pairs (prefill) of the units computed. The oracle's store writes the same
+    rows on every pass, so it runs in place on the workload's host pools.
     """
     import oracle
 
@@ -566,37 +600,52 @@ def cpu_baseline(wl, budget_s: float):
         blas = 1
     st = wl.steps[-1]
     k_len = st.num_cached + st.num_new
-    secs, keys, pairs, seqs_done, passes = 0.0, 0, 0, 0, 0
+    units = []  # (sequence, rows or None)
+    for s in range(st.batch):
+        ql = int(st.num_new[s])
+        if st.kind == "decode" or ql <= CPU_ROWS:
+            units.append((s, None))
+        else:
+            units.extend((s, np.arange(r0, min(ql, r0 + CPU_ROWS))) for r0 in range(0, ql, CPU_ROWS))
+    secs, keys, pairs, units_done, passes = 0.0, 0, 0, 0, 0
     while secs < budget_s:
         t0 = time.perf_counter()
         meta = oracle.build_metadata(st.block_table, st.num_cached, st.num_new, wl.block_size)
         oracle.store_kvcache(wl.k_cache, wl.v_cache, st.k, st.v, meta["slot_mapping"])
         secs += time.perf_counter() - t0
-        for s in range(st.batch):
+        for s, rows in units:
             t1 = time.perf_counter()
             if st.kind == "decode":
                 oracle.decode(st.q, wl.k_cache, wl.v_cache, meta["context_lens"], st.block_table, wl.scale,
                               wl.dtype, seqs=[s])
             else:
                 oracle.prefill_varlen(st.q, wl.k_cache, wl.v_cache, meta["cu_seqlens_q"], meta["cu_seqlens_k"],
-                                      st.block_table, wl.scale, wl.dtype, seqs=[s])
+                                      st.block_table, wl.scale, wl.dtype, seqs=[s],
+                                      rows=None if rows is None else {s: rows})
             secs += time.perf_counter() - t1
-            seqs_done += 1
+            units_done += 1
             keys += int(k_len[s])
             ql = int(st.num_new[s])
-            pairs += ql * (int(k_len[s]) - ql) + ql * (ql + 1) // 2
+            past = int(k_len[s]) - ql
+            r = np.arange(ql) if rows is None else rows
+            pairs += int(np.sum(past + r + 1))
             if secs > budget_s:
                 break
         passes += 1
     kv_tok = 2 * wl.num_kv_heads * wl.head_dim * wl.elem_bytes
     if st.kind == "decode":
         value, unit = keys * kv_tok / secs / 1e9, "GB/s"
+        what = f"{units_done} sequence decodes ({keys} keys)"
     else:
         value, unit = 4 * wl.head_dim * wl.num_heads * pairs / secs / 1e12, "TFLOP/s"
-    return {"value": round(value, 4), "unit": unit, "cores": int(blas), "kind": "oracle",
+        what = f"{units_done} units of up to {CPU_ROWS} query rows of a sequence ({pairs} query-key pairs)"
+    return {"value": round(value, 6), "unit": unit, "cores": int(blas), "kind": "oracle",
             "host_cpus": len(os.sched_getaffinity(0)),
             "sample": f"{passes} pass(es) of oracle metadata + store + float64 attention over the same step; "
-                      f"{seqs_done} sequence attentions ({keys} keys) in {secs:.1f} s; cores = BLAS threads"}
+                      f"{what} in {secs:.1f} s; cores = BLAS threads"}
+
+
+CPU_ROWS = 128  # query rows per unit of the prefill CPU baseline
 
 
 # ---------------------------------------------------------------------------------------------- main
@@ -619,11 +668,11 @@ def bench_one(name: str, steps: int, warmup: int, n_layers: int, out_dtype_name:
         launch_bytes = work["attn_bytes"] + (work["append_bytes"] if g.append else 0)
         step_bytes = launch_bytes if g.append else work["attn_bytes"] + work["store_bytes"] + work["meta_bytes"]
         res["launch_bytes"] = launch_bytes
-        res["attn_GBps"] = launch_bytes / (t["attn_ms"] * 1e-3) / 1e9
+        res["attn_GBps"] = launch_bytes / (t["launch_ms"] * 1e-3) / 1e9
         res["attn_frac_hbm"] = res["attn_GBps"] / HBM_PEAK_GBS
         res["step_GBps"] = step_bytes / (t["wall_ms_per_step"] * 1e-3) / 1e9
     else:
-        res["attn_TFLOPs"] = work["flops"] / (t["attn_ms"] * 1e-3) / 1e12
+        res["attn_TFLOPs"] = work["flops"] / (t["launch_ms"] * 1e-3) / 1e12
         res["attn_frac_mfma"] = res["attn_TFLOPs"] / MFMA_BF16_PEAK_TFLOPS
         res["step_TFLOPs"] = work["flops"] / (t["wall_ms_per_step"] * 1e-3) / 1e12
     if not g.append and fused_store:
@@ -633,6 +682,24 @@ def bench_one(name: str, steps: int, warmup: int, n_layers: int, out_dtype_name:
     del g
     torch.cuda.empty_cache()
     return wl, res
+
+
+def roofline_of(name: str, r: dict) -> dict:
+    """The roofline object of one workload's attention call: algorithmic bytes (decode) or flops (prefill) per
+    launch over the launch time of the uninstrumented attention-only pass, against the MI355X peak; traffic = HBM
+    bytes per launch from the committed counter summary of the same kernel sources (None if absent or stale)."""
+    t = r["timing"]
+    traffic = _traffic(f"{name}_hbm_traffic.json", _src_sha(*ATTN_SOURCES[r["kind"]]))
+    if r["kind"] == "decode":
+        return {"bound": "hbm", "achieved": round(r["attn_GBps"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(r["attn_frac_hbm"], 4), "traffic": traffic,
+                "kernel": ("pa_decode_append (" if r["append"] else "pa_decode (") +
+                          " + ".join(ATTN_KERNELS["decode"]) + ")",
+                "bytes_per_launch": r["launch_bytes"], "launch_ms": round(t["launch_ms"], 5)}
+    return {"bound": "mfma", "achieved": round(r["attn_TFLOPs"], 1), "peak": MFMA_BF16_PEAK_TFLOPS,
+            "unit": "TFLOP/s", "frac": round(r["attn_frac_mfma"], 4), "traffic": traffic,
+            "kernel": "pa_prefill_varlen (" + " + ".join(ATTN_KERNELS["prefill"]) + ")",
+            "flops_per_launch": r["work"]["flops"], "launch_ms": round(t["launch_ms"], 5)}
 
 
 def _step_text(is_dec: bool, append: bool, fused: bool) -> str:
@@ -662,6 +729,8 @@ def main() -> int:
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work for the CPU baseline")
+    ap.add_argument("--secondary-cpu-budget", type=float, default=5.0,
+                    help="seconds of oracle work for each secondary workload's CPU baseline")
     ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"), default=None,
                     help="write the HBM traffic summary of --only's workload from two rocprofv3 counter files "
                          "(no GPU needed) and exit")
@@ -673,7 +742,8 @@ def main() -> int:
     ap.add_argument("--sample-sweep", action="store_true",
                     help="only time the sampler at the Qwen3 vocabulary for batch 1, 64, 256")
     ap.add_argument("--graph-ladder", action="store_true",
-                    help="only time a decode step eager vs captured in a HIP graph over batch sizes 1..256")
+                    help="only time a decode step eager vs captured in a HIP graph over the batch sizes the engine "
+                         "captures (1, 2, 4, 8, 16, 32, ..., 512)")
     ap.add_argument("--prewarm", type=float, default=PREWARM_S,
                     help="seconds of untimed steps before the warmup steps (0 for counter runs)")
     ap.add_argument("--separate-store", action="store_true",
@@ -710,7 +780,7 @@ def main() -> int:
         print(json.dumps({"sample_sweep": sample_sweep()}))
         return 0
     if args.graph_ladder:
-        print(json.dumps({"graph_ladder": graph_ladder([1, 2, 4, 8, 16, 32, 64, 128, 256])}))
+        print(json.dumps({"graph_ladder": graph_ladder(GRAPH_LADDER)}))
         return 0
     main_name = args.only or "decode_qwen3_0p6b"
     fused = not args.separate_store
@@ -721,10 +791,10 @@ def main() -> int:
     if not args.only and not args.no_secondary:
         for name in ("prefill_qwen3_8b", "chunked_qwen3_8b", "chunk256_qwen3_8b", "decode_qwen3_32b"):
             layers = 1 if name == "decode_qwen3_32b" else args.layers
-            _, r = bench_one(name, max(10, args.steps // 2), max(2, args.warmup // 2), layers, args.out_dtype,
-                             fused, append)
+            swl, r = bench_one(name, max(10, args.steps // 2), max(2, args.warmup // 2), layers, args.out_dtype,
+                               fused, append)
             print(f"[bench] {name}: {json.dumps(r['timing'])}", file=sys.stderr, flush=True)
-            entry = {"workload": name, "attn_ms": round(r["timing"]["attn_ms"], 4),
+            entry = {"workload": name, "attn_ms": round(r["timing"]["launch_ms"], 4),
                      "step_ms": round(r["timing"]["wall_ms_per_step"], 4)}
             entry.update(_store_rate(r))
             if r["kind"] == "decode":
@@ -733,6 +803,10 @@ def main() -> int:
             else:
                 entry.update({"attn_TFLOPs": round(r["attn_TFLOPs"], 1),
                               "frac_mfma": round(r["attn_frac_mfma"], 4), "flops": r["work"]["flops"]})
+            entry["roofline"] = roofline_of(name, r)
+            if not args.no_cpu_baseline:
+                entry["cpu_baseline"] = cpu_baseline(swl, args.secondary_cpu_budget)
+            del swl
             secondary.append(entry)
     if args.calibrate_copy:
         x = torch.empty(1 << 29, dtype=torch.float16, device="cuda:0").normal_()
@@ -745,22 +819,12 @@ def main() -> int:
     t = main["timing"]
     work = main["work"]
     is_dec = main["kind"] == "decode"
-    sha = _src_sha(*ATTN_SOURCES[main["kind"]])
-    traffic = _traffic(f"{main_name}_hbm_traffic.json", sha)
+    roof = roofline_of(main_name, main)
     if is_dec:
         value = main["step_GBps"]
-        roof = {"bound": "hbm", "achieved": round(main["attn_GBps"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(main["attn_frac_hbm"], 4), "traffic": traffic,
-                "kernel": ("pa_decode_append (" if main["append"] else "pa_decode (") +
-                          " + ".join(ATTN_KERNELS["decode"]) + ")",
-                "bytes_per_launch": main["launch_bytes"], "launch_ms": round(t["attn_ms"], 5)}
         unit = "GB/s"
     else:
         value = work["flops"] / (t["wall_ms_per_step"] * 1e-3) / 1e12
-        roof = {"bound": "mfma", "achieved": round(main["attn_TFLOPs"], 1), "peak": MFMA_BF16_PEAK_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(main["attn_frac_mfma"], 4), "traffic": traffic,
-                "kernel": "prefill_mfma_kernel", "flops_per_launch": work["flops"],
-                "launch_ms": round(t["attn_ms"], 5)}
         unit = "TFLOP/s"
     st = wl.steps[-1]
     line = {
@@ -775,7 +839,9 @@ def main() -> int:
                    "step": _step_text(is_dec, main["append"], fused)},
         "breakdown_ms": ({} if main["append"] else {"metadata_store": round(t["meta_ms"], 5)} if fused else
                          {"metadata": round(t["meta_ms"], 5), "store": round(t["store_ms"], 5)}) |
-                        {"attention": round(t["attn_ms"], 5), "attention_median": round(t["attn_ms_median"], 5),
+                        {"attention_alone": round(t["launch_ms"], 5),
+                         "attention_with_events": round(t["attn_ms"], 5),
+                         "attention_with_events_median": round(t["attn_ms_median"], 5),
                          "events_step": round(t["step_ms"], 5),
                          "wall_step_with_events": round(t["wall_ms_per_step_with_events"], 5)},
         **_store_rate(main),

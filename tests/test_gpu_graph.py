@@ -6,15 +6,18 @@ serves later decode steps of the same batch size whose lengths, slots, queries a
 memory (the engine captures only its decode step and replays it with new data copied into fixed tensors,
 "一个 prompt 的一生：nano-vllm 从起服务到吐出 token" §2.2.4).
 Each replay is checked bit for bit against the same calls run eagerly on a second copy of the cache pool, with
-eager work and synchronisations between replays.
+eager work and synchronisations between replays; the decode-step replays are also checked against the oracle
+(the first and the last replay of each capture, over host pools that received every replay's stores), up to
+batch 512, the largest batch the engine captures ("一个 prompt 的一生" §3.3.2).
 """
 
 import numpy as np
 import pytest
 import torch
 
+import oracle
 import paged_kv_cache_111_amd as pa
-from harness import DEV
+from harness import DEV, assert_close
 
 HQ, HKV, D, BS = 16, 8, 128, 256
 
@@ -24,16 +27,42 @@ def _bf16(rng, shape):
     return x.to(torch.bfloat16)
 
 
+def _bits(t: torch.Tensor) -> np.ndarray:
+    return t.contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+class HostMirror:
+    """The oracle's side of a captured decode step: host pools that receive every replay's stores through the
+    oracle's store_kvcache, and the oracle's decode of a replay's step over them."""
+
+    def __init__(self, pool_k: torch.Tensor, pool_v: torch.Tensor, table: np.ndarray):
+        self.kc, self.vc = _bits(pool_k).copy(), _bits(pool_v).copy()
+        self.table = table
+
+    def store(self, k_new: torch.Tensor, v_new: torch.Tensor, slots: np.ndarray) -> None:
+        oracle.store_kvcache(self.kc, self.vc, _bits(k_new), _bits(v_new), slots)
+
+    def check(self, out: torch.Tensor, q: torch.Tensor, ctx: np.ndarray, kc_dev: torch.Tensor, what: str) -> None:
+        ref = oracle.decode(_bits(q), self.kc, self.vc, ctx, self.table, 1.0 / np.sqrt(D), "bf16")
+        assert np.array_equal(_bits(kc_dev.cpu()), self.kc), f"{what}: K pool differs from the oracle's"
+        assert_close(out, ref, what=what)
+
+
+def _slots(table: np.ndarray, pos: np.ndarray) -> np.ndarray:
+    return (table[np.arange(len(pos)), pos // BS].astype(np.int64) * BS + pos % BS).astype(np.int32)
+
+
 @pytest.mark.gpu
-@pytest.mark.parametrize("batch,split", [(1, 0), (4, 0), (16, 0), (8, 256)])
+@pytest.mark.parametrize("batch,split", [(1, 0), (4, 0), (16, 0), (8, 256), (512, 0)])
 def test_graph_store_decode_replays(batch, split):
     rng = np.random.default_rng(900 + batch + split)
-    mbps = 8                                   # up to 2048 keys per sequence
+    mbps = 4 if batch > 64 else 8              # up to 1024 (2048) keys per sequence
     nb = batch * mbps + 4
     perm = rng.permutation(nb).astype(np.int32)
     table = perm[: batch * mbps].reshape(batch, mbps)
     pool_k = _bf16(rng, (nb, BS, HKV, D))
     pool_v = _bf16(rng, (nb, BS, HKV, D))
+    host = HostMirror(pool_k, pool_v, table)
     kc_g, vc_g = pool_k.to(DEV), pool_v.to(DEV)
     kc_e, vc_e = kc_g.clone(), vc_g.clone()
 
@@ -50,14 +79,16 @@ def test_graph_store_decode_replays(batch, split):
     ws_g = torch.empty(max(need, 16), dtype=torch.uint8, device=DEV)
     ws_e = torch.empty_like(ws_g)
     scale = 1.0 / np.sqrt(D)
+    cur = {}
 
     def draw():
         lens = rng.integers(1, mbps * BS + 1, size=batch).astype(np.int32)
-        pos = lens - 1
-        sl = (table[np.arange(batch), pos // BS].astype(np.int64) * BS + pos % BS).astype(np.int32)
-        q.copy_(_bf16(rng, (batch, HQ, D)).to(DEV))
-        k_new.copy_(_bf16(rng, (batch, HKV, D)).to(DEV))
-        v_new.copy_(_bf16(rng, (batch, HKV, D)).to(DEV))
+        sl = _slots(table, lens - 1)
+        cur.update(q=_bf16(rng, (batch, HQ, D)), k=_bf16(rng, (batch, HKV, D)), v=_bf16(rng, (batch, HKV, D)),
+                   lens=lens, slots=sl)
+        q.copy_(cur["q"].to(DEV))
+        k_new.copy_(cur["k"].to(DEV))
+        v_new.copy_(cur["v"].to(DEV))
         slots.copy_(torch.from_numpy(sl).to(DEV))
         ctx.copy_(torch.from_numpy(lens).to(DEV))
         torch.cuda.synchronize()
@@ -71,11 +102,15 @@ def test_graph_store_decode_replays(batch, split):
     with torch.cuda.graph(g):
         step(kc_g, vc_g, out_g, ws_g)
     torch.cuda.synchronize()
-    for r in range(4):
+    n_rep = 4
+    for r in range(n_rep):
         if r > 0:
             draw()
         g.replay()
         torch.cuda.synchronize()
+        host.store(cur["k"], cur["v"], cur["slots"])
+        if r in (0, n_rep - 1):
+            host.check(out_g, cur["q"], cur["lens"], kc_g, what=f"batch {batch} replay {r}")
         step(kc_e, vc_e, out_e, ws_e)
         torch.cuda.synchronize()
         assert torch.isfinite(out_e).all(), f"replay {r}: eager output not finite"
@@ -84,17 +119,18 @@ def test_graph_store_decode_replays(batch, split):
 
 
 @pytest.mark.gpu
-@pytest.mark.parametrize("batch", [1, 8, 64])
+@pytest.mark.parametrize("batch", [1, 8, 64, 512])
 def test_graph_fused_metadata_store_decode_replays(batch):
     """The decode step as the engine runs it, metadata and store in one launch (pa_build_metadata_store) and then
     the balanced decode, captured once and replayed with new cached lengths, queries and K/V."""
     rng = np.random.default_rng(950 + batch)
-    mbps = 8
+    mbps = 4 if batch > 64 else 8
     nb = batch * mbps + 4
     perm = rng.permutation(nb).astype(np.int32)
     table = perm[: batch * mbps].reshape(batch, mbps)
     pool_k = _bf16(rng, (nb, BS, HKV, D))
     pool_v = _bf16(rng, (nb, BS, HKV, D))
+    host = HostMirror(pool_k, pool_v, table)
     kc_g, vc_g = pool_k.to(DEV), pool_v.to(DEV)
     kc_e, vc_e = kc_g.clone(), vc_g.clone()
 
@@ -110,12 +146,15 @@ def test_graph_fused_metadata_store_decode_replays(batch):
     ws_g = torch.empty(max(need, 16), dtype=torch.uint8, device=DEV)
     ws_e = torch.empty_like(ws_g)
     scale = 1.0 / np.sqrt(D)
+    cur = {}
 
     def draw():
         cached = rng.integers(0, mbps * BS, size=batch).astype(np.int32)   # the new token fits the table
-        q.copy_(_bf16(rng, (batch, HQ, D)).to(DEV))
-        k_new.copy_(_bf16(rng, (batch, HKV, D)).to(DEV))
-        v_new.copy_(_bf16(rng, (batch, HKV, D)).to(DEV))
+        cur.update(q=_bf16(rng, (batch, HQ, D)), k=_bf16(rng, (batch, HKV, D)), v=_bf16(rng, (batch, HKV, D)),
+                   lens=cached + 1, slots=_slots(table, cached))
+        q.copy_(cur["q"].to(DEV))
+        k_new.copy_(cur["k"].to(DEV))
+        v_new.copy_(cur["v"].to(DEV))
         num_cached.copy_(torch.from_numpy(cached).to(DEV))
         torch.cuda.synchronize()
 
@@ -129,11 +168,16 @@ def test_graph_fused_metadata_store_decode_replays(batch):
     with torch.cuda.graph(g):
         meta_g = step(kc_g, vc_g, out_g, ws_g)
     torch.cuda.synchronize()
-    for r in range(4):
+    n_rep = 4
+    for r in range(n_rep):
         if r > 0:
             draw()
         g.replay()
         torch.cuda.synchronize()
+        host.store(cur["k"], cur["v"], cur["slots"])
+        if r in (0, n_rep - 1):
+            assert np.array_equal(meta_g["slot_mapping"].cpu().numpy(), cur["slots"])
+            host.check(out_g, cur["q"], cur["lens"], kc_g, what=f"batch {batch} replay {r}")
         meta_e = step(kc_e, vc_e, out_e, ws_e)
         torch.cuda.synchronize()
         assert torch.isfinite(out_e).all(), f"replay {r}: eager output not finite"
@@ -144,17 +188,20 @@ def test_graph_fused_metadata_store_decode_replays(batch):
 
 
 @pytest.mark.gpu
-@pytest.mark.parametrize("batch", [1, 8, 64])
+@pytest.mark.parametrize("batch", [1, 8, 64, 512])
 def test_graph_decode_append_replays(batch):
     """pa_decode_append (slots from the table, store and attention in the decode's two launches) captured once and
     replayed with new cached lengths, queries and K/V; each replay must equal, bit for bit, the metadata + store
-    launch followed by pa_decode run eagerly on a second pool (the same arithmetic over the same lengths)."""
+    launch followed by pa_decode run eagerly on a second pool (the same arithmetic over the same lengths), and
+    the first and last replays the oracle."""
     rng = np.random.default_rng(970 + batch)
-    mbps = 8
+    mbps = 4 if batch > 64 else 8
     nb = batch * mbps + 4
     perm = rng.permutation(nb).astype(np.int32)
     table = perm[: batch * mbps].reshape(batch, mbps)
-    kc_g, vc_g = _bf16(rng, (nb, BS, HKV, D)).to(DEV), _bf16(rng, (nb, BS, HKV, D)).to(DEV)
+    pool_k, pool_v = _bf16(rng, (nb, BS, HKV, D)), _bf16(rng, (nb, BS, HKV, D))
+    host = HostMirror(pool_k, pool_v, table)
+    kc_g, vc_g = pool_k.to(DEV), pool_v.to(DEV)
     kc_e, vc_e = kc_g.clone(), vc_g.clone()
 
     q = torch.empty((batch, HQ, D), dtype=torch.bfloat16, device=DEV)
@@ -169,12 +216,15 @@ def test_graph_decode_append_replays(batch):
     ws_g = torch.empty(max(need, 16), dtype=torch.uint8, device=DEV)
     ws_e = torch.empty_like(ws_g)
     scale = 1.0 / np.sqrt(D)
+    cur = {}
 
     def draw():
         cached = rng.integers(0, mbps * BS, size=batch).astype(np.int32)
-        q.copy_(_bf16(rng, (batch, HQ, D)).to(DEV))
-        k_new.copy_(_bf16(rng, (batch, HKV, D)).to(DEV))
-        v_new.copy_(_bf16(rng, (batch, HKV, D)).to(DEV))
+        cur.update(q=_bf16(rng, (batch, HQ, D)), k=_bf16(rng, (batch, HKV, D)), v=_bf16(rng, (batch, HKV, D)),
+                   lens=cached + 1, slots=_slots(table, cached))
+        q.copy_(cur["q"].to(DEV))
+        k_new.copy_(cur["k"].to(DEV))
+        v_new.copy_(cur["v"].to(DEV))
         num_cached.copy_(torch.from_numpy(cached).to(DEV))
         torch.cuda.synchronize()
 
@@ -184,11 +234,15 @@ def test_graph_decode_append_replays(batch):
         pa.decode_append(q, k_new, v_new, kc_g, vc_g, num_cached, bt, scale, out=out_g, workspace=ws_g,
                          fallback=False)
     torch.cuda.synchronize()
-    for r in range(4):
+    n_rep = 4
+    for r in range(n_rep):
         if r > 0:
             draw()
         g.replay()
         torch.cuda.synchronize()
+        host.store(cur["k"], cur["v"], cur["slots"])
+        if r in (0, n_rep - 1):
+            host.check(out_g, cur["q"], cur["lens"], kc_g, what=f"batch {batch} replay {r}")
         meta = pa.build_metadata_store(num_cached, num_new, bt, batch, k_new, v_new, kc_e, vc_e)
         pa.decode(q, kc_e, vc_e, meta["context_lens"], bt, scale, out=out_e, workspace=ws_e)
         torch.cuda.synchronize()
@@ -283,7 +337,8 @@ def test_workspace_contents_do_not_matter(kind):
 @pytest.mark.gpu
 def test_graph_prefill_with_key_splits_replays():
     """The key-split prefill (split count and grids from host sizes only) captured once and replayed with new
-    queries and cache contents: every replay equals the eager call bit for bit."""
+    queries and cache contents: every replay equals the eager call bit for bit, and the first and last the
+    oracle."""
     rng = np.random.default_rng(996)
     mbps, q_len = 40, 200
     k_len = mbps * BS
@@ -301,10 +356,13 @@ def test_graph_prefill_with_key_splits_replays():
     out_e = torch.empty_like(out_g)
     scale = 1.0 / np.sqrt(D)
 
+    cur = {}
+
     def draw():
-        kc.copy_(_bf16(rng, tuple(kc.shape)).to(DEV))
-        vc.copy_(_bf16(rng, tuple(vc.shape)).to(DEV))
-        q.copy_(_bf16(rng, tuple(q.shape)).to(DEV))
+        cur.update(k=_bf16(rng, tuple(kc.shape)), v=_bf16(rng, tuple(vc.shape)), q=_bf16(rng, tuple(q.shape)))
+        kc.copy_(cur["k"].to(DEV))
+        vc.copy_(cur["v"].to(DEV))
+        q.copy_(cur["q"].to(DEV))
         torch.cuda.synchronize()
 
     draw()
@@ -317,6 +375,10 @@ def test_graph_prefill_with_key_splits_replays():
             draw()
         g.replay()
         torch.cuda.synchronize()
+        if r in (0, 2):
+            ref = oracle.prefill_varlen(_bits(cur["q"]), _bits(cur["k"]), _bits(cur["v"]), np.array([0, q_len]),
+                                        np.array([0, k_len]), table.cpu().numpy(), scale, "bf16")
+            assert_close(out_g, ref, what=f"prefill replay {r}")
         pa.prefill_varlen(q, kc, vc, cu_q, cu_k, table, q_len, k_len, scale, out=out_e, workspace=ws_e)
         torch.cuda.synchronize()
         assert torch.isfinite(out_e).all()

@@ -1,7 +1,9 @@
 """Pins of the oracle's sampler (oracle/sampler.py) to facts outside its own code.
 
-The pages give the method (temperature, softmax, Gumbel-max), not numbers, and no published test vectors of the
-generator are used, so the pins are: the distribution of the sampled token against softmax(l / T) (chi-square
+The pages give the method (temperature, softmax, Gumbel-max), not numbers. The generator is pinned by the
+known-answer vectors its authors publish with their reference implementation (Random123, file kat_vectors,
+entries "philox4x32 10"), which fix the word order, both multipliers, the key schedule and the round count. The
+sampler is pinned by the distribution of the sampled token against softmax(l / T) (chi-square
 over many independent rows), the limits and identities of the temperature (greedy at 0, l / T at 1 equals the
 sample at T), the uniformity and avalanche of the generator, exact representability of the uniforms, and the
 tie rule. A flipped Gumbel sign, a temperature that multiplies, plain exponential noise in place of the Gumbel
@@ -19,6 +21,68 @@ import oracle.sampler as osamp
 def _softmax(x):
     e = np.exp(x - x.max())
     return e / e.sum()
+
+
+# ------------------------------------------------------------------------------------------ generator identity
+
+# Philox4x32-10 known answers: (counter words 0..3, key words 0..1) -> output words 0..3. Source: the known-answer
+# vectors distributed with Random123 (Salmon, Moraes, Dror, Shaw, "Parallel random numbers: as easy as 1, 2, 3",
+# SC 2011), entries for philox4x32 with 10 rounds: an all-zero input, an all-ones input, and the digits of pi.
+PHILOX4X32_10_KAT = [
+    ((0x00000000, 0x00000000, 0x00000000, 0x00000000), (0x00000000, 0x00000000),
+     (0x6627E8D5, 0xE169C58D, 0xBC57AC4C, 0x9B00DBD8)),
+    ((0xFFFFFFFF, 0xFFFFFFFF, 0xFFFFFFFF, 0xFFFFFFFF), (0xFFFFFFFF, 0xFFFFFFFF),
+     (0x408F276D, 0x41C83B0E, 0xA20BC7C6, 0x6D5451FD)),
+    ((0x243F6A88, 0x85A308D3, 0x13198A2E, 0x03707344), (0xA4093822, 0x299F31D0),
+     (0xD16CFE09, 0x94FDCCEB, 0x5001E420, 0x24126EA1)),
+]
+
+
+@pytest.mark.parametrize("ctr,key,want", PHILOX4X32_10_KAT)
+def test_philox_matches_published_known_answers(ctr, key, want):
+    got = osamp.philox4x32_10(*(np.array([c], dtype=np.uint64) for c in ctr), key[0], key[1])
+    assert tuple(int(w[0]) for w in got) == want
+
+
+def test_philox_known_answers_in_a_batch():
+    """The vectorised form gives each lane its own answer (no mixing across array elements)."""
+    ctr = np.array([c for c, _, _ in PHILOX4X32_10_KAT], dtype=np.uint64).T
+    for j, (_, key, want) in enumerate(PHILOX4X32_10_KAT):
+        got = osamp.philox4x32_10(ctr[0], ctr[1], ctr[2], ctr[3], key[0], key[1])
+        assert tuple(int(w[j]) for w in got) == want
+
+
+@pytest.mark.parametrize("mistake", ["swap_outputs", "key_bump", "nine_rounds"])
+def test_planted_generator_mistakes_fail_the_known_answers(mistake, monkeypatch):
+    """A generator with its output words permuted, a wrong key-bump constant or one round short (each of which
+    the statistical pins below would pass) misses the published answers."""
+    if mistake == "swap_outputs":
+        real = osamp.philox4x32_10
+
+        def gen(*a):
+            x0, x1, x2, x3 = real(*a)
+            return x1, x0, x3, x2
+    elif mistake == "key_bump":
+        monkeypatch.setattr(osamp, "W1", 0xBB67AE86)
+        gen = osamp.philox4x32_10
+    else:
+        def gen(c0, c1, c2, c3, k0, k1):
+            # nine rounds: undo the tenth by running the definition with the round count changed
+            x0, x1, x2, x3 = (np.asarray(c, dtype=np.uint64) for c in (c0, c1, c2, c3))
+            ka, kb = np.uint64(k0), np.uint64(k1)
+            for r in range(9):
+                if r:
+                    ka = (ka + np.uint64(osamp.W0)) & np.uint64(osamp.MASK32)
+                    kb = (kb + np.uint64(osamp.W1)) & np.uint64(osamp.MASK32)
+                p0, p1 = x0 * np.uint64(osamp.M0), x2 * np.uint64(osamp.M1)
+                x0, x1, x2, x3 = ((p1 >> np.uint64(32)) ^ x1 ^ ka, p1 & np.uint64(osamp.MASK32),
+                                  (p0 >> np.uint64(32)) ^ x3 ^ kb, p0 & np.uint64(osamp.MASK32))
+            return tuple(w.astype(np.uint32) for w in (x0, x1, x2, x3))
+    misses = 0
+    for ctr, key, want in PHILOX4X32_10_KAT:
+        got = gen(*(np.array([c], dtype=np.uint64) for c in ctr), key[0], key[1])
+        misses += tuple(int(w[0]) for w in got) != want
+    assert misses == len(PHILOX4X32_10_KAT)
 
 
 # ------------------------------------------------------------------------------------------ distribution
