@@ -210,6 +210,13 @@ pa_status pa_norm_rope_store_kvcache(const void* k, int64_t k_tok_stride, const 
  * up to 32 ranges of at least 1024 keys, chosen from the host sizes alone, and a second launch merges the
  * ranges' partial results with the log-sum-exp rule; the workspace then holds those partials (scratch: its
  * contents do not matter between calls). Results agree to rounding with and without splits.
+ * Precision of the bf16 head_dim-128 kernel: q K^T multiplies the bf16 inputs exactly (bf16 matrix cores, float32
+ * accumulation); the softmax weights and V enter the PV product as fp16 (float32 accumulation). V is converted
+ * from bf16 to fp16 rounding toward zero: exact for magnitudes in [2^-14, 65504] (a bf16 significand fits an
+ * fp16 one); larger finite magnitudes become +-65504; magnitudes in [2^-24, 2^-14) become fp16 subnormals
+ * (truncated toward zero) and smaller ones zero. The weights (at most 256 before normalisation) are rounded to
+ * nearest fp16, and the normaliser is the sum of the rounded weights. Other dtypes and head sizes compute in
+ * float32 throughout.
  */
 pa_status pa_prefill_varlen(const void* q, int64_t q_tok_stride, const void* k_cache, const void* v_cache,
                             const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, const int32_t* block_table,
@@ -219,7 +226,7 @@ pa_status pa_prefill_varlen(const void* q, int64_t q_tok_stride, const void* k_c
                             void* out, pa_dtype out_dtype, void* workspace, size_t workspace_bytes, void* stream);
 
 /* Workspace bytes pa_prefill_varlen needs for these host sizes: 0 unless the call splits its keys (then
- * batch * ceil(max_seqlen_q / 128) * num_heads * splits * 128 rows of 132 floats). The query sees no dtype: for
+ * batch * ceil(max_seqlen_q / 128) * 128 * num_heads * splits rows of 132 floats). The query sees no dtype: for
  * head_dim 128 it answers for the bf16 kernel, and an fp32 call of the same sizes leaves the workspace unused. */
 size_t pa_prefill_workspace_bytes(int32_t batch, int32_t num_heads, int32_t head_dim, int32_t max_seqlen_q,
                                   int32_t max_seqlen_k);

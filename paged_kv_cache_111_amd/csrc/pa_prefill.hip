@@ -1,8 +1,12 @@
 // Paged varlen causal prefill on the matrix cores: bf16, head_dim 128.
 //
-// Workgroup = (sequence s, query head h, tile of 128 query rows); four waves of 32 rows each. Keys are walked in
-// tiles of 64 gathered through the block table into LDS (row-major, both K and V, double-buffered: the next
-// tile's global loads are in flight in registers while the current tile is computed), shared by the four waves:
+// Workgroup = (sequence s, KV head, a block of query rows, a group of HW query heads of that KV head); four waves
+// of 32 rows x one query head each. HW is 4 when the GQA group size G is a multiple of 4 (one 32-row block,
+// four heads: every wave has the same rows, so all four meet the causal diagonal at the same key tile), 2 when
+// G is even (two 32-row blocks x two heads) and 1 otherwise (four 32-row blocks of one head). All waves of a
+// workgroup read one KV head, so the K/V tiles a workgroup stages serve all of them. Keys are walked in tiles of
+// 64 gathered through the block table into LDS (row-major, both K and V, double-buffered: the next tile's global
+// loads are in flight in registers while the current tile is computed):
 //   S^T[key, q] = K[key, :] . Q[q, :]      32x32x16 MFMA, A = K rows from LDS, B = Q^T kept in registers
 //   O^T[d, q]  += V^T[d, key] P^T[key, q]  32x32x16 fp16 MFMA, A = V^T via the LDS transpose read (V is
 //                                           converted to fp16 when staged), B = P^T (fp16) formed
@@ -18,10 +22,12 @@
 // scores), so cache contents there cannot reach the output.
 //
 // Workgroup order: the flat grid is renumbered so that the workgroups the hardware sends to one XCD (every
-// eighth) get consecutive logical ids, and the logical order is (KV head, query tile from the last, sequence,
-// query head in the group). The G query heads that share a KV head, and the query tiles of that head, then run
-// on one XCD and read the same K/V through its L2; the last (heaviest, under the causal mask) query tiles of
-// all sequences start first, so the short tail of light tiles balances the finish.
+// eighth) get consecutive logical ids, and the logical order is (KV head, group of hw row blocks = 128 rows from
+// the last, sequence, row block in the group, head group). The row blocks of one KV head run on one XCD and read
+// the same K/V through its L2, and the blocks of a 128-row group start together and walk the same keys (with
+// four heads per workgroup, ordering the blocks one by one across sequences instead ran the varlen workload 25%
+// slower); the last (heaviest, under the causal mask) groups of all sequences start first, so the short tail of
+// light blocks balances the finish.
 #include <algorithm>
 #include <type_traits>
 
@@ -29,39 +35,49 @@
 
 namespace pa {
 
-constexpr int kPreRows = 128;  // query rows per workgroup
+constexpr int kPreRows = 128;  // query rows x heads per workgroup (4 waves x 32 rows)
 constexpr int kPartRow = 132;  // floats per row of a split partial: m, l, two unused, O[128] (16-byte aligned)
+
+// Query heads per workgroup for a GQA group of G heads (see the header comment).
+inline int prefill_heads_per_wg(int G) { return G % 4 == 0 ? 4 : (G % 2 == 0 ? 2 : 1); }
 
 template <bool kAligned, bool kPow2>
 __global__ __launch_bounds__(kPreThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_mfma_kernel(
     const uint16_t* __restrict__ q, int64_t q_stride, const uint16_t* __restrict__ k_cache,
     const uint16_t* __restrict__ v_cache, const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k,
     const int32_t* __restrict__ block_table, int32_t mbps, int32_t batch, int32_t Hq, int32_t Hkv, int32_t bs,
-    int32_t bs_shift, float scale_log2, void* __restrict__ out, int out_bf16, int32_t n_qtiles, int32_t n_work,
-    int32_t n_splits, float* __restrict__ part) {
-  // ---- which (KV head, sequence, query tile, key split, query head) this workgroup computes
+    int32_t bs_shift, float scale_log2, void* __restrict__ out, int out_bf16, int32_t hw, int32_t n_qtiles,
+    int32_t n_work, int32_t n_splits, int32_t part_rows, float* __restrict__ part) {
+  // ---- which (KV head, sequence, row block, key split, head group) this workgroup computes
   const int per_xcd = (int(gridDim.x) + 7) >> 3;
   const int logical = int(blockIdx.x & 7) * per_xcd + int(blockIdx.x >> 3);
   if (logical >= n_work) return;
   const int G = Hq / Hkv;
-  const int gi = logical % G;
-  int rest = logical / G;
+  const int n_hg = G / hw;
+  const int rows = kPreRows / hw;  // query rows of the workgroup: 32 x (4 / hw)
+  const int hg = logical % n_hg;
+  int rest = logical / n_hg;
   const int sp = rest % n_splits;
   rest /= n_splits;
+  // row blocks in groups of hw (128 rows): the blocks of a group are consecutive ids, so they start together and
+  // walk the same keys through the XCD's L2 (as the G one-head workgroups of a 128-row block would); groups go
+  // from the last (heaviest under the causal mask)
+  const int qsub = rest % hw;
+  rest /= hw;
   const int s = rest % batch;
   rest /= batch;
-  const int qtile = n_qtiles - 1 - rest % n_qtiles;
-  const int kvh = rest / n_qtiles;
-  const int h = kvh * G + gi;
+  const int n_grp = n_qtiles / hw;
+  const int qtile = (n_grp - 1 - rest % n_grp) * hw + (hw - 1 - qsub);
+  const int kvh = rest / n_grp;
 
   const int q0 = cu_q[s];
   const int q_len = cu_q[s + 1] - q0;
-  const int row0 = qtile * kPreRows;
+  const int row0 = qtile * rows;
   if (row0 >= q_len) return;
   const int k_len = cu_k[s + 1] - cu_k[s];
   const int past = k_len - q_len;  // position of row 0
-  const int row_end = min(q_len, row0 + kPreRows);
-  const int n_keys = past + row_end;  // keys needed by the last row of the tile
+  const int row_end = min(q_len, row0 + rows);
+  const int n_keys = past + row_end;  // keys needed by the last row of the block
   const int n_tiles_all = (n_keys + kPreKeys - 1) / kPreKeys;
   // Split sp of n_splits takes key tiles [t0, t1) of the workgroup's tiles (all of them when n_splits == 1); its
   // loads stop at key t1 * 64, and its rows leave unnormalised partials for the merge pass.
@@ -70,25 +86,25 @@ __global__ __launch_bounds__(kPreThreads) __attribute__((amdgpu_waves_per_eu(2, 
   const int t1 = min(n_tiles_all, t0 + per_split);
   const int n_tiles = t1 - t0;
   const int k_lim = min(k_len, t1 * kPreKeys);
-  // first row of this workgroup's partials (split mode only): [item][split][row][kPartRow]
-  const int64_t prow0 =
-      ((int64_t((int64_t(s) * n_qtiles + qtile) * Hq + (kvh * G + gi)) * n_splits + sp) * kPreRows) * kPartRow;
-  if (n_tiles <= 0) {  // an empty split (only when n_splits > 1): its rows' partials say "no keys"
-    const int r = int(threadIdx.x);
-    if (r < kPreRows && row0 + r < q_len) {
-      part[prow0 + int64_t(r) * kPartRow] = -INFINITY;
-      part[prow0 + int64_t(r) * kPartRow + 1] = 0.f;
-    }
-    return;
-  }
 
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int lr = lane & 31;   // query column owned by this lane
   const int hh = lane >> 5;   // wave half
-  const int my_row = row0 + 32 * w + lr;
-  const int wave_row0 = row0 + 32 * w;
+  const int h = kvh * G + hg * hw + w % hw;  // this wave's query head
+  const int wave_row0 = row0 + 32 * (w / hw);
+  const int my_row = wave_row0 + lr;
+  // partial row of (sequence, row, head, split): [batch][part_rows][Hq][n_splits][kPartRow] (split mode only)
+  auto prow = [&]() { return ((int64_t(s) * part_rows + my_row) * Hq + h) * n_splits + sp; };
+  if (n_tiles <= 0) {  // an empty split (only when n_splits > 1): its rows' partials say "no keys"
+    if (hh == 0 && my_row < q_len) {
+      part[prow() * kPartRow] = -INFINITY;
+      part[prow() * kPartRow + 1] = 0.f;
+    }
+    return;
+  }
+
   const int wave_keys = wave_row0 < q_len ? past + min(q_len - 1, wave_row0 + 31) + 1 : 0;
   const int wave_tiles = (wave_keys + kPreKeys - 1) / kPreKeys;  // the tiles this wave computes: 0 .. wave_tiles-1
   const int32_t* table = block_table + int64_t(s) * mbps;
@@ -127,33 +143,34 @@ __global__ __launch_bounds__(kPreThreads) __attribute__((amdgpu_waves_per_eu(2, 
   const int va_off = (4 * (g4 >> 1) + (li >> 2)) * kVRow + 16 * (g4 & 1) + 4 * (li & 3);
 
   u32x4 kst[kPieces], vst[kPieces];
+#define PF_GLOAD(dst, b, kb) pf_gload1<kAligned, kPow2>(dst, b, table, kb, k_lim, bs, bs_shift, row_bytes, tid)
   // prologue: K tiles t0 and t0+1, V tile t0 in LDS (their loads issued together: one round trip); scores of
   // tile t0
   {
     u32x4 k1st[kPieces];
     const int kb0 = t0 * kPreKeys;
-    pf_gload1<kAligned, kPow2>(kst, kbase, table, kb0, k_lim, bs, bs_shift, row_bytes, tid);
-    pf_gload1<kAligned, kPow2>(vst, vbase, table, kb0, k_lim, bs, bs_shift, row_bytes, tid);
-    pf_gload1<kAligned, kPow2>(k1st, kbase, table, kb0 + kPreKeys, k_lim, bs, bs_shift, row_bytes, tid);
+    PF_GLOAD(kst, kbase, kb0);
+    PF_GLOAD(vst, vbase, kb0);
+    PF_GLOAD(k1st, kbase, kb0 + kPreKeys);
     pf_lstore_k(kst, kt[0], tid);
     pf_lstore_v(vst, vt[0], tid);
     pf_lstore_k(k1st, kt[1], tid);
   }
   __syncthreads();
   f32x16 sa[kSub], sb[kSub];
-  pf_scores(sa, kt[0], ka_off, qb);
+  pf_scores<kAligned>(sa, kt[0], ka_off, qb);
   __syncthreads();  // K tile t0 has been read by every wave before the first step replaces it
 
   auto step = [&](int j, f32x16 (&cur)[kSub], f32x16 (&nxt)[kSub], auto par) {
     constexpr int P = decltype(par)::value;  // (j - t0) % 2
     const int kb = j * kPreKeys;
     // K tile j+2 and V tile j+1 start loading (past the split's end they read as zero and touch no memory)
-    pf_gload1<kAligned, kPow2>(kst, kbase, table, kb + 2 * kPreKeys, k_lim, bs, bs_shift, row_bytes, tid);
-    pf_gload1<kAligned, kPow2>(vst, vbase, table, kb + kPreKeys, k_lim, bs, bs_shift, row_bytes, tid);
+    PF_GLOAD(kst, kbase, kb + 2 * kPreKeys);
+    PF_GLOAD(vst, vbase, kb + kPreKeys);
     if (j < wave_tiles) {
       if (kb + kPreKeys - 1 > past + wave_row0) pf_mask(cur, my_pos - kb - 4 * hh);
       const float mh = pf_halfmax(cur) * scale_log2;
-      pf_scores(nxt, kt[1 - P], ka_off, qb);  // tile j+1's scores (K tile j+1 has been in LDS since the last step)
+      pf_scores<kAligned>(nxt, kt[1 - P], ka_off, qb);  // tile j+1's scores (K tile j+1 has been in LDS since the last step)
       // The reference max only moves when the row max would exceed it by more than the slack; until then the
       // weights exp2(s - m) stay below 2^8 and O, l need no rescaling. The result O / l does not depend on m.
       // The row's keys are split over the two wave halves: the vote runs on each half's own max (no half above
@@ -188,7 +205,7 @@ __global__ __launch_bounds__(kPreThreads) __attribute__((amdgpu_waves_per_eu(2, 
   if (my_row >= q_len) return;
   lsum = xhalf_sum(lsum);
   if (n_splits > 1) {  // unnormalised partial: m (scaled log2 units), l, O; the merge pass finishes the row
-    float* pr = part + prow0 + int64_t(my_row - row0) * kPartRow;
+    float* pr = part + prow() * kPartRow;
     if (hh == 0) {
       pr[0] = m;
       pr[1] = lsum;
@@ -224,7 +241,8 @@ __global__ __launch_bounds__(kPreThreads) __attribute__((amdgpu_waves_per_eu(2, 
 
 // Key splits of a call (host sizes only): when the grid holds fewer workgroups than the chip runs at once (two per
 // CU on the 256 CUs), each workgroup's key tiles are split so that about that many run, each split at least
-// kMinSplitKeys keys, at most kMaxSplits splits. One split leaves the output to the attention kernel itself.
+// kMinSplitKeys keys, at most kMaxSplits splits. One split leaves the output to the attention kernel itself. The
+// count is taken on 128-row units of work (row blocks x heads / 128), which is the same for every GQA packing.
 constexpr int64_t kPrefillSlots = 512;
 constexpr int64_t kMinSplitKeys = 1024;
 constexpr int64_t kMaxSplits = 32;
@@ -239,17 +257,19 @@ int32_t prefill_splits(int32_t batch, int32_t max_seqlen_q, int32_t max_seqlen_k
   return int32_t(std::max<int64_t>(sp, 1));
 }
 
+// Rows of one sequence in the partial layout: max_seqlen_q rounded up to 128 (a multiple of every packing's block).
+static int64_t prefill_part_rows(int32_t max_seqlen_q) { return (int64_t(max_seqlen_q) + kPreRows - 1) / kPreRows * kPreRows; }
+
 size_t prefill_mfma_workspace_bytes(int32_t batch, int32_t max_seqlen_q, int32_t max_seqlen_k, int32_t Hq) {
   const int32_t sp = prefill_splits(batch, max_seqlen_q, max_seqlen_k, Hq);
   if (sp <= 1) return 0;
-  const int64_t n_qtiles = (int64_t(max_seqlen_q) + kPreRows - 1) / kPreRows;
-  return size_t(int64_t(batch) * n_qtiles * Hq * sp * kPreRows * kPartRow) * sizeof(float);
+  return size_t(int64_t(batch) * prefill_part_rows(max_seqlen_q) * Hq * sp * kPartRow) * sizeof(float);
 }
 
 // Merge of a row's split partials: M = max m_i, L = sum l_i 2^(m_i - M), O = sum O_i 2^(m_i - M) / L (splits with
 // no key for the row have m = -inf and weight 0). One wave per (token, query head), two of the 128 d per lane.
 __global__ __launch_bounds__(64) void prefill_merge_kernel(const int32_t* __restrict__ cu_q, int32_t batch, int32_t Hq,
-                                                           int32_t n_qtiles, int32_t n_splits,
+                                                           int32_t part_rows, int32_t n_splits,
                                                            const float* __restrict__ part, void* __restrict__ out,
                                                            int out_bf16) {
   const int t = blockIdx.x;
@@ -261,12 +281,9 @@ __global__ __launch_bounds__(64) void prefill_merge_kernel(const int32_t* __rest
     if (cu_q[mid] <= t) a = mid; else b = mid;
   }
   const int r = t - cu_q[a];
-  const int qtile = r / kPreRows;
-  const int row = r - qtile * kPreRows;
-  const int64_t sstride = int64_t(kPreRows) * kPartRow;
-  const float* p = part + ((int64_t((int64_t(a) * n_qtiles + qtile) * Hq + h) * n_splits) * kPreRows + row) * kPartRow;
-  const float mj = lane < n_splits ? p[lane * sstride] : -INFINITY;
-  const float lj = lane < n_splits ? p[lane * sstride + 1] : 0.f;
+  const float* p = part + ((int64_t(a) * part_rows + r) * Hq + h) * n_splits * kPartRow;
+  const float mj = lane < n_splits ? p[lane * kPartRow] : -INFINITY;
+  const float lj = lane < n_splits ? p[lane * kPartRow + 1] : 0.f;
   const float M = wave_max(mj);  // split 0 holds key 0, which every row sees: M is finite
   const float wj = mj == -INFINITY ? 0.f : exp2f(mj - M);
   const float L = wave_sum(wj * lj);
@@ -274,7 +291,7 @@ __global__ __launch_bounds__(64) void prefill_merge_kernel(const int32_t* __rest
   for (int j = 0; j < n_splits; ++j) {
     const float w = __shfl(wj, j, 64);
     if (w != 0.f) {  // wave-uniform; a split without keys for the row left no O
-      const float2 v = *reinterpret_cast<const float2*>(p + j * sstride + 4 + 2 * lane);
+      const float2 v = *reinterpret_cast<const float2*>(p + j * kPartRow + 4 + 2 * lane);
       a0 += w * v.x;
       a1 += w * v.y;
     }
@@ -293,10 +310,13 @@ void launch_prefill_mfma(const void* q, int64_t q_stride, const void* k_cache, c
                          int32_t batch, int32_t total_q, int32_t max_seqlen_q, int32_t max_seqlen_k, int32_t Hq,
                          int32_t Hkv, int32_t block_size, float scale, void* out, bool out_bf16, void* workspace,
                          hipStream_t stream) {
-  const int n_qtiles = (max_seqlen_q + kPreRows - 1) / kPreRows;
+  const int hw = prefill_heads_per_wg(Hq / Hkv);
+  const int rows = kPreRows / hw;
+  const int n_qtiles = (max_seqlen_q + kPreRows - 1) / kPreRows * hw;  // a multiple of hw: 128-row groups
   const int n_splits = prefill_splits(batch, max_seqlen_q, max_seqlen_k, Hq);
-  const int n_work = batch * n_qtiles * Hq * n_splits;
+  const int n_work = batch * n_qtiles * (Hq / hw) * n_splits;
   const int grid = ((n_work + 7) / 8) * 8;
+  const int part_rows = int(prefill_part_rows(max_seqlen_q));
   const float sl2 = scale * kLog2e;
   const bool pow2 = (block_size & (block_size - 1)) == 0;
   const bool aligned = block_size % kPreKeys == 0;
@@ -308,8 +328,8 @@ void launch_prefill_mfma(const void* q, int64_t q_stride, const void* k_cache, c
   float* part = static_cast<float*>(workspace);
 #define PA_LAUNCH_PF(A, P)                                                                                      \
   hipLaunchKernelGGL((prefill_mfma_kernel<A, P>), dim3(grid), dim3(kPreThreads), 0, stream, qp, q_stride, kc, vc, \
-                     cu_q, cu_k, block_table, mbps, batch, Hq, Hkv, block_size, shift, sl2, out, int(out_bf16),  \
-                     n_qtiles, n_work, n_splits, part)
+                     cu_q, cu_k, block_table, mbps, batch, Hq, Hkv, block_size, shift, sl2, out, int(out_bf16), hw, \
+                     n_qtiles, n_work, n_splits, part_rows, part)
   if (aligned && pow2) PA_LAUNCH_PF(true, true);
   else if (aligned) PA_LAUNCH_PF(true, false);
   else if (pow2) PA_LAUNCH_PF(false, true);
@@ -317,7 +337,7 @@ void launch_prefill_mfma(const void* q, int64_t q_stride, const void* k_cache, c
 #undef PA_LAUNCH_PF
   if (n_splits > 1)
     hipLaunchKernelGGL(prefill_merge_kernel, dim3(unsigned(total_q), unsigned(Hq)), dim3(64), 0, stream, cu_q, batch,
-                       Hq, n_qtiles, n_splits, part, out, int(out_bf16));
+                       Hq, part_rows, n_splits, part, out, int(out_bf16));
 }
 
 }  // namespace pa

@@ -90,16 +90,27 @@ __device__ __forceinline__ void pf_lstore_v(const u32x4* src, uint16_t* vt, int 
 }
 
 // S^T for the 64 keys of a K tile in LDS: sc[sub][i] is key 32 sub + 8 (i / 4) + 4 hh + (i % 4) of the tile,
-// query column lr of the wave.
+// query column lr of the wave. With kBatch, a sub-tile's eight K operands are read before its MFMAs (eight LDS
+// reads in flight instead of two; the per-key gathers of unaligned block sizes leave no registers for it).
+template <bool kBatch>
 __device__ __forceinline__ void pf_scores(f32x16 (&sc)[kSub], const uint16_t* kt, int ka_off, const bf16x8 (&qb)[8]) {
 #pragma unroll
   for (int sub = 0; sub < kSub; ++sub) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) sc[sub][i] = 0.f;
     const uint16_t* ka = kt + ka_off + 32 * sub * kKRow;
+    if (kBatch) {
+      u32x4 kr[8];
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks)
-      sc[sub] = mfma32x32x16(as_bf16x8(*reinterpret_cast<const u32x4*>(ka + 16 * ks)), qb[ks], sc[sub]);
+      for (int ks = 0; ks < 8; ++ks) kr[ks] = *reinterpret_cast<const u32x4*>(ka + 16 * ks);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) sc[sub] = mfma32x32x16(as_bf16x8(kr[ks]), qb[ks], sc[sub]);
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks)
+        sc[sub] = mfma32x32x16(as_bf16x8(*reinterpret_cast<const u32x4*>(ka + 16 * ks)), qb[ks], sc[sub]);
+    }
   }
 }
 

@@ -10,8 +10,8 @@ import torch
 
 import oracle
 import paged_kv_cache_111_amd as pa
-from harness import DEV, DevStep, assert_bf16_is_rounded_f32, assert_close, compare_metadata, flat_rows, hip_step, i32, \
-    oracle_step, to_dev, to_host_bits
+from harness import DEV, MAX_ABS, REL_RMS, DevStep, assert_bf16_is_rounded_f32, assert_close, compare_metadata, \
+    flat_rows, hip_step, i32, oracle_step, to_dev, to_host_bits
 from workloads import build_decode, build_prefill, make_config
 
 pytestmark = pytest.mark.gpu
@@ -503,3 +503,69 @@ def test_metadata_large_batch_bit_exact():
     ref = oracle.build_metadata(table, cached, new, bs)
     meta = pa.build_metadata(i32(cached), i32(new), i32(table), int(new.sum()), len(perm), bs)
     compare_metadata(meta, ref)
+
+
+# ------------------------------------------------------------------------------------------------ PV precision
+
+
+def _f16_toward_zero(x: np.ndarray) -> np.ndarray:
+    """float32 -> the fp16 value rounding toward zero, as float32: finite magnitudes above 65504 become +-65504,
+    magnitudes below 2^-14 fp16 subnormals (truncated) or zero. Written from the IEEE half format with NumPy's
+    float16 (round to nearest), stepped one ulp toward zero where that rounded away from zero."""
+    x = np.asarray(x, dtype=np.float32)
+    with np.errstate(over="ignore"):
+        h = x.astype(np.float16)
+    away = np.abs(h.astype(np.float32)) > np.abs(x)
+    h = np.where(away, np.nextafter(h, np.float16(0)), h)
+    h = np.where(np.abs(x) > 65504, np.sign(x).astype(np.float16) * np.float16(65504), h)
+    return h.astype(np.float32)
+
+
+@pytest.mark.parametrize("mode", ["large", "tiny"])
+def test_prefill_pv_range_rule(mode):
+    """The bf16 head_dim-128 prefill runs its PV product in fp16 with V converted toward zero (the rule stated in
+    pa.h for pa_prefill_varlen). V holding +-1e5 entries (beyond fp16's 65504) or only magnitudes near 1e-6 (fp16
+    subnormals): the output follows the oracle run on the converted V, and differs from the oracle on the raw V
+    by far more than that, so the rule is what the kernel computes."""
+    wl = build_prefill("pv_range", 731, 8, 2, 128, 64, "bf16", [320], [128], num_blocks=12)
+    st = wl.steps[0]
+    rng = np.random.default_rng(5)
+
+    def f32(bits):
+        return (bits.astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+    def bits(x):
+        return torch.from_numpy(np.asarray(x, np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(
+            np.uint16)
+
+    vp, vn = f32(wl.v_cache), f32(st.v)
+    if mode == "large":
+        for a in (vp, vn):
+            hit = rng.random(a.shape) < 0.05
+            a[hit] = np.sign(rng.standard_normal(int(hit.sum()))) * 1e5
+    else:
+        vp *= 1e-6
+        vn *= 1e-6
+    wl.v_cache[...] = bits(vp)
+    st.v[...] = bits(vn)
+    kc_h, vc_h = wl.k_cache.copy(), wl.v_cache.copy()
+    kc, vc = to_dev(wl.k_cache, wl.dtype), to_dev(wl.v_cache, wl.dtype)
+    print(f"[case] pv_range {mode}", flush=True)
+    meta_d, out = hip_step(wl, DevStep(st, wl.dtype), kc, vc)
+    torch.cuda.synchronize()
+    meta_r, plain = oracle_step(wl, st, kc_h, vc_h)
+    compare_metadata(meta_d, meta_r)
+    rule = oracle.prefill_varlen(f32(st.q), f32(kc_h), _f16_toward_zero(f32(vc_h)), meta_r["cu_seqlens_q"],
+                                 meta_r["cu_seqlens_k"], st.block_table, wl.scale, "f32")
+    got = out.float().cpu().numpy().astype(np.float64)
+
+    def rel(a, b):
+        return float(np.sqrt(np.sum((a - b) ** 2) / np.sum(b * b)))
+
+    r_rule, r_plain = rel(got, rule), rel(got, plain)
+    print(f"[err] pv_range {mode}: rel_rms vs rule {r_rule:.2e}, vs raw V {r_plain:.2e}", flush=True)
+    assert r_rule <= REL_RMS, f"{mode}: output is not the stated rule's ({r_rule:.3g})"
+    assert r_plain > 5 * max(r_rule, 1e-3), f"{mode}: the rule is not observable ({r_plain:.3g} vs {r_rule:.3g})"
+    # elementwise: the fp16 weights (relative 2^-11 each) bound the error by 2^-11 of the largest |V'| reached
+    bound = MAX_ABS + 2.0 ** -11 * float(np.max(np.abs(_f16_toward_zero(f32(vc_h)))))
+    assert np.max(np.abs(got - rule)) <= bound
