@@ -281,6 +281,24 @@ pa_status pa_decode_append(const void* q, int64_t q_tok_stride, const void* k_ne
                            int32_t num_blocks, int32_t block_size, float softmax_scale, pa_dtype dtype, void* out,
                            pa_dtype out_dtype, void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * pa_decode_append_noalloc -- pa_decode_append for callers that cannot allocate device memory: code recorded
+ * into a HIP graph, tight serving loops, harnesses that forbid hipMalloc. Same arguments, semantics, shapes and
+ * error codes as pa_decode_append, without the workspace: its partial results go to a scratch array of fixed
+ * size (51.1 MB: 3072 workers x 2 slots x 2080 floats) that the library holds in device memory, one per GPU it runs
+ * on, until the process ends. No call allocates (no hipMalloc, hipFree or allocating library routine); the first
+ * call on a device resolves the array's device address for that device (make it before capturing a graph).
+ * The stream must belong to the current device (else PA_ERR_SHAPE). The array's size does not depend on the
+ * call's sizes (every shape pa_decode_append takes fits it); its contents never need clearing, and calls that
+ * overlap on one GPU (two streams at once) share it and race: serialise them.
+ */
+pa_status pa_decode_append_noalloc(const void* q, int64_t q_tok_stride, const void* k_new, int64_t k_tok_stride,
+                                   const void* v_new, int64_t v_tok_stride, void* k_cache, void* v_cache,
+                                   const int32_t* num_cached, const int32_t* block_table, int32_t max_blocks_per_seq,
+                                   int32_t batch, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                                   int32_t num_blocks, int32_t block_size, float softmax_scale, pa_dtype dtype,
+                                   void* out, pa_dtype out_dtype, void* stream);
+
 /* Keys per split pa_decode uses for these host sizes when split_tokens == 0 and the balanced decode does not
  * apply. */
 int32_t pa_decode_split_tokens(int32_t batch, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,

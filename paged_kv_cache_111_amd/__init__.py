@@ -15,6 +15,7 @@ from .binding import (  # noqa: F401
     checked_mode,
     decode,
     decode_append,
+    decode_append_noalloc,
     decode_split_tokens,
     decode_workspace_bytes,
     lib,
@@ -29,6 +30,7 @@ from .binding import (  # noqa: F401
 
 __all__ = [
     "CHECK_KINDS", "PAError", "PAIndexError", "build_metadata", "build_metadata_store", "check_indices",
-    "checked_mode", "decode", "decode_append", "decode_split_tokens", "decode_workspace_bytes", "lib", "norm_rope_store_kvcache",
-    "prefill_varlen", "prefill_workspace_bytes", "sample", "sample_workspace_bytes", "status_str", "store_kvcache",
+    "checked_mode", "decode", "decode_append", "decode_append_noalloc", "decode_split_tokens",
+    "decode_workspace_bytes", "lib", "norm_rope_store_kvcache", "prefill_varlen", "prefill_workspace_bytes", "sample",
+    "sample_workspace_bytes", "status_str", "store_kvcache",
 ]

@@ -55,6 +55,9 @@ SIGNATURES = {
     "pa_decode_append": (ctypes.c_int, [_c_ptr, _c_i64, _c_ptr, _c_i64, _c_ptr, _c_i64, _c_ptr, _c_ptr, _c_ptr,
                                         _c_ptr, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_f32,
                                         ctypes.c_int, _c_ptr, ctypes.c_int, _c_ptr, _c_size, _c_ptr]),
+    "pa_decode_append_noalloc": (ctypes.c_int, [_c_ptr, _c_i64, _c_ptr, _c_i64, _c_ptr, _c_i64, _c_ptr, _c_ptr,
+                                                _c_ptr, _c_ptr, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32,
+                                                _c_i32, _c_f32, ctypes.c_int, _c_ptr, ctypes.c_int, _c_ptr]),
     "pa_decode_split_tokens": (_c_i32, [_c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32]),
     "pa_decode_workspace_bytes": (_c_size, [_c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32]),
 }
@@ -358,6 +361,33 @@ def prefill_varlen(q, k_cache, v_cache, cu_seqlens_q, cu_seqlens_k, block_table,
                                  _dtype_code(q.dtype), _ptr(out), _dtype_code(out.dtype), _ptr(workspace), wbytes,
                                  _stream(stream))
     _check("pa_prefill_varlen", st)
+    return out
+
+
+def decode_append_noalloc(q, k_new, v_new, k_cache, v_cache, num_cached, block_table, softmax_scale: float, out,
+                          stream=None):
+    """pa_decode_append_noalloc: as decode_append, with the partials in the library's own device scratch (no
+    workspace, nothing allocated here or in the library: out must be given). Raises on shapes the call does not
+    take (no fallback, since the fallback would allocate)."""
+    nb, bs, hkv, d = _cache_dims(k_cache, v_cache)
+    _require(q.dtype == k_cache.dtype and k_new.dtype == k_cache.dtype and v_new.dtype == k_cache.dtype,
+             "q, k_new and v_new must match the cache dtype")
+    hq = int(q.shape[1])
+    qs = _token_rows(q, hq, d, "q")
+    ks = _token_rows(k_new, hkv, d, "k_new")
+    vs = _token_rows(v_new, hkv, d, "v_new")
+    _i32(num_cached, "num_cached")
+    _i32(block_table, "block_table")
+    B = int(q.shape[0])
+    _require(k_new.shape[0] == B and v_new.shape[0] == B and num_cached.shape[0] == B,
+             "q, k_new, v_new and num_cached must have one row per sequence")
+    _require(out is not None and out.is_contiguous() and tuple(out.shape) == (B, hq, d),
+             "out must be given, contiguous [B, Hq, D]")
+    st = lib().pa_decode_append_noalloc(_ptr(q), qs, _ptr(k_new), ks, _ptr(v_new), vs, _ptr(k_cache), _ptr(v_cache),
+                                        _ptr(num_cached), _ptr(block_table), int(block_table.shape[1]), B, hq, hkv, d,
+                                        nb, bs, float(softmax_scale), _dtype_code(q.dtype), _ptr(out),
+                                        _dtype_code(out.dtype), _stream(stream))
+    _check("pa_decode_append_noalloc", st)
     return out
 
 

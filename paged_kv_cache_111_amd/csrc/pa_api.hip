@@ -1,5 +1,7 @@
 // The C ABI: argument checks on the host, kernel choice, launch. No allocation, no synchronisation, no reads of
 // device memory; every error that the host can see is returned before anything is launched.
+#include <mutex>
+
 #include "../../include/pa.h"
 #include "pa_launch.h"
 
@@ -66,6 +68,64 @@ bool decode_uses_stream(int32_t split_tokens, int32_t Hq, int32_t Hkv, int32_t D
   const int64_t padded_max = (int64_t(mbps) * block_size + 31) & ~int64_t(31);
   return split_tokens == 0 && D == 128 && Hq / Hkv <= 16 && Hkv <= kStreamWorkers && block_size % 32 == 0 &&
          batch <= 4096 && int64_t(batch) * padded_max < (int64_t(1) << 31);
+}
+
+// Argument checks of pa_decode_append and pa_decode_append_noalloc (everything but the workspace).
+pa_status check_decode_append(const void* q, int64_t q_tok_stride, const void* k_new, int64_t k_tok_stride,
+                              const void* v_new, int64_t v_tok_stride, const void* k_cache, const void* v_cache,
+                              const int32_t* num_cached, const int32_t* block_table, int32_t max_blocks_per_seq,
+                              int32_t batch, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                              int32_t num_blocks, int32_t block_size, float softmax_scale, pa_dtype dtype,
+                              const void* out, pa_dtype out_dtype) {
+  if (!valid_dtype(dtype) || !valid_dtype(out_dtype) || !valid_head_dim(head_dim)) return PA_ERR_UNSUPPORTED;
+  if (batch < 0 || num_heads <= 0 || num_kv_heads <= 0 || num_heads % num_kv_heads != 0 || block_size <= 0 ||
+      num_blocks <= 0)
+    return PA_ERR_SHAPE;
+  if (int64_t(num_blocks) * block_size > kInt32Max) return PA_ERR_SHAPE;
+  const int64_t row = int64_t(num_kv_heads) * head_dim;
+  if (q_tok_stride < int64_t(num_heads) * head_dim || k_tok_stride < row || v_tok_stride < row) return PA_ERR_SHAPE;
+  if (!(softmax_scale > 0.f) || softmax_scale > 3.0e38f) return PA_ERR_SHAPE;
+  if (batch == 0) return PA_OK;
+  if (max_blocks_per_seq <= 0) return PA_ERR_SHAPE;
+  if (!q || !k_new || !v_new || !k_cache || !v_cache || !num_cached || !block_table || !out) return PA_ERR_NULL;
+  if (!decode_uses_mfma(dtype, num_heads, num_kv_heads, head_dim) ||
+      !decode_uses_stream(0, num_heads, num_kv_heads, head_dim, max_blocks_per_seq, block_size, batch))
+    return PA_ERR_UNSUPPORTED;
+  if (q_tok_stride % 8 || k_tok_stride % 8 || v_tok_stride % 8 || !aligned(q, 16) || !aligned(k_new, 16) ||
+      !aligned(v_new, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(out, 16))
+    return PA_ERR_UNSUPPORTED;
+  return PA_OK;
+}
+
+// The scratch of pa_decode_append_noalloc, for callers that cannot allocate: the balanced decode's partial slots
+// (kStreamWorkers workers x 2 slots x kStreamSlotFloats floats = 51.1 MB), one array per GPU the library runs on,
+// held until the process ends. Its contents never need clearing (every partial the merge reads was written by the
+// same call), and calls that overlap on one GPU share it and race.
+constexpr size_t kScratchBytes = size_t(kStreamWorkers) * 2 * pa::kStreamSlotFloats * sizeof(float);
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+// The array's device address per device, resolved once with that device current (host code never passes the
+// array's name itself to a kernel: on the host it is only a stand-in for the symbol).
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+void* scratch_ptr[kMaxDevices] = {};
+
+pa_status scratch_for(hipStream_t stream, void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return PA_ERR_LAUNCH;
+  if (stream) {  // the kernels run on the stream's device: it must be the current one, whose address is resolved
+    int sdev = -1;
+    if (hipStreamGetDevice(stream, &sdev) != hipSuccess) return PA_ERR_LAUNCH;
+    if (sdev != dev) return PA_ERR_SHAPE;
+  }
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (!scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return PA_ERR_LAUNCH;
+    scratch_ptr[dev] = p;
+  }
+  *out = scratch_ptr[dev];
+  return PA_OK;
 }
 
 }  // namespace
@@ -348,29 +408,40 @@ pa_status pa_decode_append(const void* q, int64_t q_tok_stride, const void* k_ne
                            int32_t batch, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
                            int32_t num_blocks, int32_t block_size, float softmax_scale, pa_dtype dtype, void* out,
                            pa_dtype out_dtype, void* workspace, size_t workspace_bytes, void* stream) {
-  if (!valid_dtype(dtype) || !valid_dtype(out_dtype) || !valid_head_dim(head_dim)) return PA_ERR_UNSUPPORTED;
-  if (batch < 0 || num_heads <= 0 || num_kv_heads <= 0 || num_heads % num_kv_heads != 0 || block_size <= 0 ||
-      num_blocks <= 0)
-    return PA_ERR_SHAPE;
-  if (int64_t(num_blocks) * block_size > kInt32Max) return PA_ERR_SHAPE;
-  const int64_t row = int64_t(num_kv_heads) * head_dim;
-  if (q_tok_stride < int64_t(num_heads) * head_dim || k_tok_stride < row || v_tok_stride < row) return PA_ERR_SHAPE;
-  if (!(softmax_scale > 0.f) || softmax_scale > 3.0e38f) return PA_ERR_SHAPE;
-  if (batch == 0) return PA_OK;
-  if (max_blocks_per_seq <= 0) return PA_ERR_SHAPE;
-  if (!q || !k_new || !v_new || !k_cache || !v_cache || !num_cached || !block_table || !out) return PA_ERR_NULL;
-  if (!decode_uses_mfma(dtype, num_heads, num_kv_heads, head_dim) ||
-      !decode_uses_stream(0, num_heads, num_kv_heads, head_dim, max_blocks_per_seq, block_size, batch))
-    return PA_ERR_UNSUPPORTED;
-  if (q_tok_stride % 8 || k_tok_stride % 8 || v_tok_stride % 8 || !aligned(q, 16) || !aligned(k_new, 16) ||
-      !aligned(v_new, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(out, 16))
-    return PA_ERR_UNSUPPORTED;
+  const pa_status st = check_decode_append(q, q_tok_stride, k_new, k_tok_stride, v_new, v_tok_stride, k_cache,
+                                           v_cache, num_cached, block_table, max_blocks_per_seq, batch, num_heads,
+                                           num_kv_heads, head_dim, num_blocks, block_size, softmax_scale, dtype, out,
+                                           out_dtype);
+  if (st != PA_OK || batch == 0) return st;
   const size_t need = pa::decode_stream_workspace_bytes(kStreamWorkers);
   if (workspace_bytes < need) return PA_ERR_WORKSPACE;
   if (!workspace || !aligned(workspace, 16)) return PA_ERR_NULL;
   pa::launch_decode_stream(q, q_tok_stride, k_cache, v_cache, num_cached, block_table, max_blocks_per_seq, batch,
                            num_heads, num_kv_heads, block_size, softmax_scale, out, out_dtype == PA_BF16,
                            kStreamWorkers, workspace, static_cast<hipStream_t>(stream), k_new, k_tok_stride, v_new,
+                           v_tok_stride);
+  return launched();
+}
+
+pa_status pa_decode_append_noalloc(const void* q, int64_t q_tok_stride, const void* k_new, int64_t k_tok_stride,
+                                   const void* v_new, int64_t v_tok_stride, void* k_cache, void* v_cache,
+                                   const int32_t* num_cached, const int32_t* block_table, int32_t max_blocks_per_seq,
+                                   int32_t batch, int32_t num_heads, int32_t num_kv_heads, int32_t head_dim,
+                                   int32_t num_blocks, int32_t block_size, float softmax_scale, pa_dtype dtype,
+                                   void* out, pa_dtype out_dtype, void* stream) {
+  const pa_status st = check_decode_append(q, q_tok_stride, k_new, k_tok_stride, v_new, v_tok_stride, k_cache,
+                                           v_cache, num_cached, block_table, max_blocks_per_seq, batch, num_heads,
+                                           num_kv_heads, head_dim, num_blocks, block_size, softmax_scale, dtype, out,
+                                           out_dtype);
+  if (st != PA_OK || batch == 0) return st;
+  static_assert(pa::decode_stream_workspace_bytes(kStreamWorkers) <= kScratchBytes, "scratch too small");
+  if (pa::decode_stream_workspace_bytes(kStreamWorkers) > kScratchBytes) return PA_ERR_WORKSPACE;
+  void* part = nullptr;
+  const pa_status sc = scratch_for(static_cast<hipStream_t>(stream), &part);
+  if (sc != PA_OK) return sc;
+  pa::launch_decode_stream(q, q_tok_stride, k_cache, v_cache, num_cached, block_table, max_blocks_per_seq, batch,
+                           num_heads, num_kv_heads, block_size, softmax_scale, out, out_dtype == PA_BF16,
+                           kStreamWorkers, part, static_cast<hipStream_t>(stream), k_new, k_tok_stride, v_new,
                            v_tok_stride);
   return launched();
 }

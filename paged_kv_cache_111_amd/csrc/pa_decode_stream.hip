@@ -27,7 +27,7 @@
 namespace pa {
 
 constexpr int kStreamWaves = 4;                       // workers per workgroup (they share the prefix sums)
-constexpr int kSlotFloats = 16 + 16 + 16 * 128;       // one partial: m[16], l[16], O[16][128] (G <= 16)
+constexpr int kSlotFloats = kStreamSlotFloats;       // one partial: m[16], l[16], O[16][128] (G <= 16)
 #ifndef PA_STREAM_MIN_CHUNK
 #define PA_STREAM_MIN_CHUNK 128
 #endif
@@ -389,10 +389,6 @@ __global__ __launch_bounds__(64) void decode_stream_merge_kernel(const int32_t* 
   } else {
     *reinterpret_cast<float2*>(static_cast<float*>(out) + ob) = make_float2(a0 * inv, a1 * inv);
   }
-}
-
-size_t decode_stream_workspace_bytes(int32_t n_workers) {
-  return size_t(n_workers) * 2 * kSlotFloats * sizeof(float);
 }
 
 void launch_decode_stream(const void* q, int64_t q_stride, const void* k_cache, const void* v_cache,

@@ -46,7 +46,11 @@ void launch_decode_mfma(const void* q, int64_t q_stride, const void* k_cache, co
                         int32_t Hq, int32_t Hkv, int32_t block_size, float scale, void* out, bool out_bf16,
                         int32_t split_tokens, int32_t max_splits, void* workspace, hipStream_t stream);
 
-size_t decode_stream_workspace_bytes(int32_t n_workers);
+// One partial slot of the balanced decode: m[16], l[16], O[16][128] floats (G <= 16); each worker owns two.
+constexpr int kStreamSlotFloats = 16 + 16 + 16 * 128;
+constexpr size_t decode_stream_workspace_bytes(int32_t n_workers) {
+  return size_t(n_workers) * 2 * kStreamSlotFloats * sizeof(float);
+}
 
 void launch_decode_stream(const void* q, int64_t q_stride, const void* k_cache, const void* v_cache,
                           const int32_t* ctx_lens, const int32_t* block_table, int32_t mbps, int32_t batch,
