@@ -141,8 +141,8 @@ def write_traffic_summary(workload: str, fetch_csv: str, write_csv: str) -> dict
         return sum(vals) / len(vals), len(vals)
 
     known_kib = (1 << 30) / 1024.0
-    copy_f, _ = mean(fetch, "vectorized_elementwise_kernel")
-    copy_w, _ = mean(write, "vectorized_elementwise_kernel")
+    copy_f, _ = mean(fetch, COPY_KERNEL)
+    copy_w, _ = mean(write, COPY_KERNEL)
     fscale, wscale = known_kib / copy_f, known_kib / copy_w
     per, total = {}, 0.0
     for kn in ATTN_KERNELS[kind]:
@@ -546,6 +546,181 @@ def store_sweep(tokens=(64, 2048, 16384, 131072), iters: int = 50):
     return rows
 
 
+STORE_PROFILE_TOKENS = 131072  # the large store of the store profile (0.6B cache shape: 2 KiB K + 2 KiB V per token)
+
+
+def store_profile(iters: int = 20):
+    """The store kernels alone, for the store counters: pa_store_kvcache of STORE_PROFILE_TOKENS tokens at the
+    Qwen3-0.6B cache shape (random distinct slots of a pool twice that size), then the varlen prefill workload's
+    metadata + store launch (pa_build_metadata_store) and its separate store (pa_store_kvcache), each `iters`
+    calls after 3 untimed ones. Returns per call: mean time between events around the calls and the algorithmic
+    bytes (K and V rows read and written, slots, and for the fused launch the metadata arrays)."""
+    import torch
+
+    import paged_kv_cache_111_amd as pa
+    from workloads import make_config
+
+    dev = "cuda:0"
+    res = {}
+
+    def timed(fn):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(iters):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / iters
+
+    Hkv, D, bs, T = 8, 128, 256, STORE_PROFILE_TOKENS
+    nb = 2 * T // bs
+    rng = np.random.default_rng(5000 + T)
+    slots = torch.from_numpy(rng.permutation(nb * bs)[:T].astype(np.int32)).to(dev)
+    gen = torch.Generator(device=dev).manual_seed(T)
+    k = torch.randn((T, Hkv, D), device=dev, generator=gen).to(torch.bfloat16)
+    v = torch.randn((T, Hkv, D), device=dev, generator=gen).to(torch.bfloat16)
+    kc = torch.zeros((nb, bs, Hkv, D), dtype=torch.bfloat16, device=dev)
+    vc = torch.zeros_like(kc)
+    us = timed(lambda: pa.store_kvcache(k, v, kc, vc, slots))
+    nbytes = 2 * (2 * T * Hkv * D * 2) + 4 * T
+    res["store_kvcache_131072"] = {"kernel": "store_kvcache_kernel", "us": round(us, 2), "bytes": nbytes,
+                                   "GBps": round(nbytes / us / 1e3, 1)}
+    del k, v, kc, vc, slots
+    torch.cuda.empty_cache()
+
+    wl = make_config("prefill_qwen3_8b")
+    g = GpuWorkload(wl, 1, torch.float32)
+    st = g.step
+    kc, vc = g.k_layers[0], g.v_layers[0]
+    work = algorithmic_work(wl, st, 4)
+    us = timed(lambda: pa.build_metadata_store(g.num_cached, g.num_new, g.block_table, g.total_q, g.k, g.v, kc, vc))
+    nbytes = work["store_bytes"] + work["meta_bytes"]
+    res["metadata_store_prefill_qwen3_8b"] = {"kernel": "metadata_store_kernel", "us": round(us, 2),
+                                              "bytes": nbytes, "GBps": round(nbytes / us / 1e3, 1),
+                                              "tokens": work["tokens"]}
+    meta = pa.build_metadata(g.num_cached, g.num_new, g.block_table, g.total_q, wl.num_blocks, wl.block_size)
+    us = timed(lambda: pa.store_kvcache(g.k, g.v, kc, vc, meta["slot_mapping"]))
+    nbytes = work["store_bytes"]
+    res["store_kvcache_prefill_qwen3_8b"] = {"kernel": "store_kvcache_kernel", "us": round(us, 2), "bytes": nbytes,
+                                             "GBps": round(nbytes / us / 1e3, 1), "tokens": work["tokens"]}
+    return res
+
+
+STORE_KERNELS = ("store_kvcache_kernel", "metadata_store_kernel")
+COPY_KERNEL = "MulFunctor"  # torch.mul over 1 GiB of fp16: the plain copy the byte counters are scaled by
+STORE_SOURCES = ("pa_meta_store.hip", "pa_common.h", "pa_api.hip")
+
+
+def _kernel_calls(path: str, names):
+    """Per dispatch, in order, the counter value of each kernel whose name contains one of `names`."""
+    import collections
+    import csv
+
+    out = collections.defaultdict(list)
+    with open(path, newline="") as f:
+        for r in csv.DictReader(f):
+            for n in names:
+                if n in r["Kernel_Name"]:
+                    out[n].append(float(r["Counter_Value"]))
+    return out
+
+
+def write_store_traffic_summary(fetch_csv: str, write_csv: str, trace_csv: str) -> dict:
+    """profiles/store_hbm_traffic.json from three rocprofv3 runs of `bench.py --store-profile`: FETCH_SIZE and
+    WRITE_SIZE (--pmc, with --calibrate-copy) and a kernel trace. For each store launch: the mean kernel duration (trace),
+    its algorithmic bytes (K/V rows read and written, slots, and the metadata arrays of the fused launch) over that
+    duration, and HBM bytes per launch (counters scaled by the 1 GiB copy's known / measured, as for the attention
+    kernels). The profile runs, in order: 3 + 20 store_kvcache calls of STORE_PROFILE_TOKENS tokens at the 0.6B
+    cache shape, 3 + 20 metadata + store launches of the varlen prefill step, 3 + 20 stores of that step's tokens;
+    the 3 untimed calls of each group are left out of the means."""
+    import csv
+
+    from workloads import make_config
+
+    names = (COPY_KERNEL,) + STORE_KERNELS
+    fetch, write = _kernel_calls(fetch_csv, names), _kernel_calls(write_csv, names)
+    known_kib = (1 << 30) / 1024.0
+    fscale = known_kib / (sum(fetch[COPY_KERNEL]) / len(fetch[COPY_KERNEL]))
+    wscale = known_kib / (sum(write[COPY_KERNEL]) / len(write[COPY_KERNEL]))
+    dur = {n: [] for n in STORE_KERNELS}
+    with open(trace_csv, newline="") as f:
+        for r in sorted(csv.DictReader(f), key=lambda r: int(r["Dispatch_Id"])):
+            for n in STORE_KERNELS:
+                if n in r["Kernel_Name"]:
+                    dur[n].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-3)  # ns -> us
+
+    def split(v):  # [large store x 23, prefill-step store x 23] for store_kvcache_kernel
+        h = len(v) // 2
+        return v[:h], v[h:]
+
+    wl = make_config("prefill_qwen3_8b", fill=False)
+    work = algorithmic_work(wl, wl.steps[-1], 4)
+    T, row = STORE_PROFILE_TOKENS, 8 * 128 * 2
+    algo = {"store_kvcache_131072": 2 * (2 * T * row) + 4 * T,
+            "store_kvcache_prefill_qwen3_8b": work["store_bytes"],
+            "metadata_store_prefill_qwen3_8b": work["store_bytes"] + work["meta_bytes"]}
+    sk_f, sk_w, sk_d = split(fetch["store_kvcache_kernel"]), split(write["store_kvcache_kernel"]), \
+        split(dur["store_kvcache_kernel"])
+    groups = {"store_kvcache_131072": ("store_kvcache_kernel", sk_f[0], sk_w[0], sk_d[0]),
+              "store_kvcache_prefill_qwen3_8b": ("store_kvcache_kernel", sk_f[1], sk_w[1], sk_d[1]),
+              "metadata_store_prefill_qwen3_8b": ("metadata_store_kernel", fetch["metadata_store_kernel"],
+                                                  write["metadata_store_kernel"], dur["metadata_store_kernel"])}
+    launches = {}
+    for key, (kern, fv, wv, dv) in groups.items():
+        fk, wk = sum(fv[3:]) / len(fv[3:]), sum(wv[3:]) / len(wv[3:])
+        us = sum(dv[3:]) / len(dv[3:])
+        hbm = (fk * fscale + wk * wscale) * 1024
+        launches[key] = {"kernel": kern, "kernel_us": round(us, 2), "algorithmic_bytes": algo[key],
+                         "GBps": round(algo[key] / us / 1e3, 1),
+                         "frac_hbm_peak": round(algo[key] / us / 1e3 / HBM_PEAK_GBS, 4),
+                         "FETCH_SIZE_KiB": round(fk, 1), "WRITE_SIZE_KiB": round(wk, 1), "hbm_bytes": int(hbm),
+                         "hbm_over_algorithmic": round(hbm / algo[key], 3), "dispatches": len(dv) - 3}
+    out = {
+        "what": "store launches: algorithmic bytes (K/V rows read and written, slots, metadata arrays) over the mean "
+                "kernel duration from the kernel trace, and HBM bytes per launch from rocprofv3 FETCH_SIZE and "
+                "WRITE_SIZE scaled by a plain 1 GiB copy's known / measured",
+        "commands": [f"cd /tmp && rocprofv3 --pmc {c} -d gpurun_out/pmc_{c}_store -o pmc --output-format csv -- "
+                     f"python /root/repo/bench.py --store-profile --calibrate-copy" for c in ("FETCH_SIZE",
+                                                                                             "WRITE_SIZE")]
+                    + ["cd /tmp && rocprofv3 --kernel-trace --stats -d gpurun_out/kt_store -o kt --output-format csv "
+                       "-- python /root/repo/bench.py --store-profile",
+                       "python bench.py --store-traffic-summary gpurun_out/pmc_FETCH_SIZE_store/"
+                       "pmc_counter_collection.csv gpurun_out/pmc_WRITE_SIZE_store/pmc_counter_collection.csv "
+                       "gpurun_out/kt_store/kt_kernel_trace.csv"],
+        "copy_kernel": {"FETCH_SIZE_KiB": round(sum(fetch[COPY_KERNEL]) / len(fetch[COPY_KERNEL]), 1),
+                        "WRITE_SIZE_KiB": round(sum(write[COPY_KERNEL]) / len(write[COPY_KERNEL]), 1),
+                        "fetch_scale": round(fscale, 4), "write_scale": round(wscale, 4)},
+        "launches": launches,
+        "source_files": list(STORE_SOURCES),
+        "source_sha": _src_sha(*STORE_SOURCES),
+    }
+    with open(os.path.join(ROOT, "profiles", "store_hbm_traffic.json"), "w", encoding="utf-8") as f:
+        json.dump(out, f, indent=1)
+        f.write("\n")
+    return out
+
+
+def write_kernel_stats_summary(name: str, stats_csv: str, command: str) -> str:
+    """profiles/<name>_kernel_stats.txt from a rocprofv3 --kernel-trace --stats kernel_stats.csv: calls, mean,
+    min and max duration and share per kernel, with the command that made the file."""
+    import csv
+
+    rows = list(csv.DictReader(open(stats_csv, newline="")))
+    lines = ["# rocprofv3 kernel statistics", f"# command: {command}", "",
+             f"{'kernel':60s} {'calls':>6s} {'avg_us':>10s} {'min_us':>10s} {'max_us':>10s} {'share_%':>8s}"]
+    for r in rows:
+        n = re.sub(r"\(.*", "", r["Name"]).replace("void ", "")
+        lines.append(f"{n[:60]:60s} {int(r['Calls']):6d} {float(r['AverageNs']) / 1e3:10.2f} "
+                     f"{float(r['MinNs']) / 1e3:10.2f} {float(r['MaxNs']) / 1e3:10.2f} {float(r['Percentage']):8.2f}")
+    text = "\n".join(lines) + "\n"
+    with open(os.path.join(ROOT, "profiles", f"{name}_kernel_stats.txt"), "w", encoding="utf-8") as f:
+        f.write(text)
+    return text
+
+
 def sample_sweep(batches=(1, 64, 256), vocab: int = 151936, iters: int = 50):
     """pa_sample at the Qwen3 vocabulary: time per call (events over back-to-back calls) and the rate at which
     it consumes logits (B·V·4 bytes; the uniforms are generated in the kernel, not read)."""
@@ -737,6 +912,13 @@ def main() -> int:
     ap.add_argument("--sq-summary", nargs=2, metavar=("PASS_A_CSV", "PASS_B_CSV"), default=None,
                     help="write the SQ counter summary of --only's workload from two rocprofv3 counter files "
                          "(no GPU needed) and exit")
+    ap.add_argument("--store-profile", action="store_true",
+                    help="only run the store launches of the store counter summary (large store, the varlen "
+                         "prefill step's metadata + store and its separate store)")
+    ap.add_argument("--store-traffic-summary", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "TRACE_CSV"),
+                    default=None, help="write profiles/store_hbm_traffic.json (no GPU needed) and exit")
+    ap.add_argument("--stats-summary", nargs=3, metavar=("NAME", "STATS_CSV", "COMMAND"), default=None,
+                    help="write profiles/NAME_kernel_stats.txt from a rocprofv3 kernel_stats.csv (no GPU needed)")
     ap.add_argument("--store-sweep", action="store_true",
                     help="only time store_kvcache at the 0.6B cache shape for 64 .. 131072 tokens")
     ap.add_argument("--sample-sweep", action="store_true",
@@ -766,6 +948,12 @@ def main() -> int:
             ap.error("--sq-summary needs --only WORKLOAD")
         print(json.dumps(write_sq_summary(args.only, *args.sq_summary), indent=1))
         return 0
+    if args.store_traffic_summary:
+        print(json.dumps(write_store_traffic_summary(*args.store_traffic_summary), indent=1))
+        return 0
+    if args.stats_summary:
+        print(write_kernel_stats_summary(*args.stats_summary))
+        return 0
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the attention step runs "
               "on one GPU's share and has no cross-GPU exchange)", file=sys.stderr)
@@ -775,6 +963,16 @@ def main() -> int:
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     if args.store_sweep:
         print(json.dumps({"store_sweep": store_sweep()}))
+        return 0
+    if args.store_profile:
+        if args.calibrate_copy:
+            x = torch.empty(1 << 29, dtype=torch.float16, device="cuda:0").normal_()
+            y = torch.empty_like(x)
+            for _ in range(3):
+                torch.mul(x, 1.0, out=y)  # reads 1 GiB, writes 1 GiB
+            torch.cuda.synchronize()
+            del x, y
+        print(json.dumps({"store_profile": store_profile()}))
         return 0
     if args.sample_sweep:
         print(json.dumps({"sample_sweep": sample_sweep()}))
