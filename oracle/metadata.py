@@ -6,8 +6,8 @@ Passages followed:
   * a sequence of n tokens occupies ceil(n / block_size) blocks, the last one holding
     n - (num_blocks - 1) * block_size tokens, and logical block i covers tokens [i*bs, (i+1)*bs)
     ("Nano-vLLM 源码逐行解析 第2篇", sequence.py: num_blocks, last_block_num_tokens, block(i));
-  * get_slots: full blocks first, then the used part of the last block ("Nano-vLLM 架构详解" §3.2, the KV cache
-    write function);
+  * get_slots: the slots of a sequence's tokens, block by block ("Nano-vLLM 架构详解" §3.2, the KV cache write
+    function), here built from the token range of each logical block and the slot formula;
   * prefill flattening: tokens of all sequences concatenated without padding, positions counted per sequence,
     cu_seqlens_q as prefix sums, slot_mapping[i] the slot of flattened token i ("一个 prompt 的一生" §3.3.2, the
     prepare_prefill example with block_size 4);
@@ -42,13 +42,13 @@ def block_token_slice(i: int, num_tokens: int, block_size: int) -> slice:
 
 
 def get_slots(block_ids, block_size: int, seq_len: int) -> list:
-    """Slots of positions 0..seq_len-1 of a sequence laid out over block_ids, block by block."""
+    """Slots of positions 0..seq_len-1 of a sequence laid out over block_ids: each logical block i holds the tokens
+    of block_token_slice(i, ...), and token t of it sits at offset t - i * block_size of physical block
+    block_ids[i] (slot formula). The blocks a sequence needs are num_blocks(seq_len, ...)."""
     slots = []
-    for b in block_ids[:-1]:
-        start = int(b) * block_size
-        slots.extend(range(start, start + block_size))
-    start = int(block_ids[-1]) * block_size
-    slots.extend(range(start, start + seq_len - (len(block_ids) - 1) * block_size))
+    for i in range(num_blocks(seq_len, block_size)):
+        toks = block_token_slice(i, seq_len, block_size)
+        slots.extend(slot_of(block_ids[i], block_size, t - i * block_size) for t in range(toks.start, toks.stop))
     return slots
 
 
