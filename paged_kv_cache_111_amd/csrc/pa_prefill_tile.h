@@ -178,9 +178,10 @@ __device__ __forceinline__ void pf_pv(const f16x8 (&pb)[kSub][2], f32x16 (&o)[4]
   }
 }
 
-// The tile's weights, then its PV product. All weights are formed before the 16 MFMAs run: vector instructions
-// placed between one wave's MFMAs stall its issue, while the other wave on the SIMD can run its vector work
-// during them.
+// The tile's weights, then its PV product. The compiler forms each k-step's weights while the previous k-step's
+// MFMAs run, which measured faster than forming all weights first (the PV block then waits on its LDS reads);
+// the score MFMAs stay one block, since weights placed between them delayed the wave's MFMAs more than the other
+// wave on the SIMD lost.
 __device__ __forceinline__ void pf_weights_pv(const f32x16 (&sc)[kSub], f32x16 (&o)[4], float m, float& lsum,
                                               const uint16_t* vt, int va_off, float scale_log2) {
   f16x8 pb[kSub][2];
