@@ -27,7 +27,9 @@
 // the same K/V through its L2, and the blocks of a 128-row group start together and walk the same keys (with
 // four heads per workgroup, ordering the blocks one by one across sequences instead ran the varlen workload 25%
 // slower); the last (heaviest, under the causal mask) groups of all sequences start first, so the short tail of
-// light blocks balances the finish.
+// light blocks balances the finish. A grid sized from max_seqlen_q holds many row blocks past a shorter
+// sequence's end; for batches of up to 64 sequences the grid is sized from total_q instead and each workgroup
+// finds the c-th existing block of that order (the same items in the same order, without the empty workgroups).
 #include <algorithm>
 #include <type_traits>
 
@@ -37,6 +39,8 @@ namespace pa {
 
 constexpr int kPreRows = 128;  // query rows x heads per workgroup (4 waves x 32 rows)
 constexpr int kPartRow = 132;  // floats per row of a split partial: m, l, two unused, O[128] (16-byte aligned)
+constexpr int kCompactBatch = 64;  // batches up to this many sequences (and prompts up to 63 x 128 rows) number only
+                                   // existing row blocks: one lane per sequence, one per 128-row group round
 
 // Query heads per workgroup for a GQA group of G heads (see the header comment).
 inline int prefill_heads_per_wg(int G) { return G % 4 == 0 ? 4 : (G % 2 == 0 ? 2 : 1); }
@@ -47,7 +51,7 @@ __global__ __launch_bounds__(kPreThreads) __attribute__((amdgpu_waves_per_eu(2, 
     const uint16_t* __restrict__ v_cache, const int32_t* __restrict__ cu_q, const int32_t* __restrict__ cu_k,
     const int32_t* __restrict__ block_table, int32_t mbps, int32_t batch, int32_t Hq, int32_t Hkv, int32_t bs,
     int32_t bs_shift, float scale_log2, void* __restrict__ out, int out_bf16, int32_t hw, int32_t n_qtiles,
-    int32_t n_work, int32_t n_splits, int32_t part_rows, float* __restrict__ part) {
+    int32_t n_work, int32_t n_splits, int32_t part_rows, float* __restrict__ part, int32_t per_kvh) {
   // ---- which (KV head, sequence, row block, key split, head group) this workgroup computes
   const int per_xcd = (int(gridDim.x) + 7) >> 3;
   const int logical = int(blockIdx.x & 7) * per_xcd + int(blockIdx.x >> 3);
@@ -55,26 +59,65 @@ __global__ __launch_bounds__(kPreThreads) __attribute__((amdgpu_waves_per_eu(2, 
   const int G = Hq / Hkv;
   const int n_hg = G / hw;
   const int rows = kPreRows / hw;  // query rows of the workgroup: 32 x (4 / hw)
-  const int hg = logical % n_hg;
-  int rest = logical / n_hg;
-  const int sp = rest % n_splits;
-  rest /= n_splits;
-  // row blocks in groups of hw (128 rows): the blocks of a group are consecutive ids, so they start together and
-  // walk the same keys through the XCD's L2 (as the G one-head workgroups of a 128-row block would); groups go
-  // from the last (heaviest under the causal mask)
-  const int qsub = rest % hw;
-  rest /= hw;
-  const int s = rest % batch;
-  rest /= batch;
   const int n_grp = n_qtiles / hw;
-  const int qtile = (n_grp - 1 - rest % n_grp) * hw + (hw - 1 - qsub);
-  const int kvh = rest / n_grp;
-
-  const int q0 = cu_q[s];
-  const int q_len = cu_q[s + 1] - q0;
+  // Row blocks in groups of hw (128 rows): the blocks of a group are consecutive ids, so they start together and
+  // walk the same keys through the XCD's L2 (as the G one-head workgroups of a 128-row block would); groups go
+  // from the last rows of the longest sequence down (heaviest under the causal mask first), and within a group
+  // round by sequence, then by block from the group's last.
+  int hg, sp, s, qtile, kvh, q0, q_len, k_len;
+  if (per_kvh > 0) {
+    // Compact numbering (batch <= 64, n_grp <= 63): the grid holds per_kvh >= the number of non-empty items of a
+    // KV head, and item c is the c-th non-empty (row block, head group, split) in the order above. One lane per
+    // sequence holds its row-block count; lane g counts the blocks of the first g group rounds, a ballot finds
+    // the round of item c, and a walk over the sequences its row block (register reads only, no LDS).
+    kvh = logical / per_kvh;
+    int c = logical % per_kvh;
+    hg = c % n_hg;
+    c /= n_hg;
+    sp = c % n_splits;
+    c /= n_splits;
+    const int lane = int(threadIdx.x) & 63;
+    const bool has = lane < batch;  // this lane's sequence: its offsets and lengths in one round trip
+    const int lq0 = has ? cu_q[lane] : 0, lq = has ? cu_q[lane + 1] - lq0 : 0, lk = has ? cu_k[lane + 1] - cu_k[lane] : 0;
+    const int nq = (lq + rows - 1) / rows;
+    int before = 0;  // lane g: blocks at or above block (n_grp - g) * hw, over all sequences
+    for (int t = 0; t < batch; ++t) before += max(0, __builtin_amdgcn_readlane(nq, t) - (n_grp - lane) * hw);
+    if (c >= __builtin_amdgcn_readlane(before, n_grp)) return;  // beyond the last non-empty item
+    const int g = __builtin_amdgcn_readfirstlane(__popcll(__ballot(lane <= n_grp && before <= c))) - 1;
+    const int base = (n_grp - 1 - g) * hw;  // lowest block of round g
+    int r = c - __builtin_amdgcn_readlane(before, g);  // position within the round
+    s = -1;
+    qtile = 0;
+    for (int t = 0; t < batch; ++t) {
+      const int cnt = min(hw, max(0, __builtin_amdgcn_readlane(nq, t) - base));  // sequence t's blocks in the round
+      if (r < cnt) {
+        s = t;
+        qtile = base + cnt - 1 - r;
+        break;
+      }
+      r -= cnt;
+    }
+    if (s < 0) return;  // not reached: the round holds more than r blocks
+    q0 = __builtin_amdgcn_readlane(lq0, s);
+    q_len = __builtin_amdgcn_readlane(lq, s);
+    k_len = __builtin_amdgcn_readlane(lk, s);
+  } else {
+    hg = logical % n_hg;
+    int rest = logical / n_hg;
+    sp = rest % n_splits;
+    rest /= n_splits;
+    const int qsub = rest % hw;
+    rest /= hw;
+    s = rest % batch;
+    rest /= batch;
+    qtile = (n_grp - 1 - rest % n_grp) * hw + (hw - 1 - qsub);
+    kvh = rest / n_grp;
+    q0 = cu_q[s];
+    q_len = cu_q[s + 1] - q0;
+    if (qtile * rows >= q_len) return;
+    k_len = cu_k[s + 1] - cu_k[s];
+  }
   const int row0 = qtile * rows;
-  if (row0 >= q_len) return;
-  const int k_len = cu_k[s + 1] - cu_k[s];
   const int past = k_len - q_len;  // position of row 0
   const int row_end = min(q_len, row0 + rows);
   const int n_keys = past + row_end;  // keys needed by the last row of the block
@@ -314,7 +357,12 @@ void launch_prefill_mfma(const void* q, int64_t q_stride, const void* k_cache, c
   const int rows = kPreRows / hw;
   const int n_qtiles = (max_seqlen_q + kPreRows - 1) / kPreRows * hw;  // a multiple of hw: 128-row groups
   const int n_splits = prefill_splits(batch, max_seqlen_q, max_seqlen_k, Hq);
-  const int n_work = batch * n_qtiles * (Hq / hw) * n_splits;
+  // Up to 64 sequences the grid counts only row blocks that exist: at most (total_q + batch (rows - 1)) / rows of
+  // them per KV head and head group, against batch x n_qtiles in the plain numbering.
+  const int n_hg = (Hq / Hkv) / hw;
+  const int64_t n_blocks = std::min<int64_t>(int64_t(batch) * n_qtiles, (int64_t(total_q) + int64_t(batch) * (rows - 1)) / rows);
+  const int per_kvh = batch <= kCompactBatch && n_qtiles / hw <= 63 ? int(n_blocks) * n_hg * n_splits : 0;
+  const int n_work = per_kvh > 0 ? per_kvh * Hkv : batch * n_qtiles * (Hq / hw) * n_splits;
   const int grid = ((n_work + 7) / 8) * 8;
   const int part_rows = int(prefill_part_rows(max_seqlen_q));
   const float sl2 = scale * kLog2e;
@@ -329,7 +377,7 @@ void launch_prefill_mfma(const void* q, int64_t q_stride, const void* k_cache, c
 #define PA_LAUNCH_PF(A, P)                                                                                      \
   hipLaunchKernelGGL((prefill_mfma_kernel<A, P>), dim3(grid), dim3(kPreThreads), 0, stream, qp, q_stride, kc, vc, \
                      cu_q, cu_k, block_table, mbps, batch, Hq, Hkv, block_size, shift, sl2, out, int(out_bf16), hw, \
-                     n_qtiles, n_work, n_splits, part_rows, part)
+                     n_qtiles, n_work, n_splits, part_rows, part, per_kvh)
   if (aligned && pow2) PA_LAUNCH_PF(true, true);
   else if (aligned) PA_LAUNCH_PF(true, false);
   else if (pow2) PA_LAUNCH_PF(false, true);

@@ -127,6 +127,14 @@ def test_decode_qwen3_32b_split_sizes(decode_32b, split):
 
 # ------------------------------------------------------------------------------------------------ small shapes
 
+def _short_prompts(seed: int, n: int):
+    """n prompts of 1..199 tokens, about half of them after a cached 16-token block (when longer than it)."""
+    rng = np.random.default_rng(seed)
+    k_lens = rng.integers(1, 200, n)
+    cached = np.minimum(rng.integers(0, 2, n) * 16, k_lens - 1)
+    return [int(x) for x in k_lens], [int(x) for x in cached]
+
+
 PREFILL_CASES = [
     # Hq, Hkv, D, bs, dtype, k_lens, cached
     (32, 8, 128, 256, "bf16", [300, 129, 1000, 17], [256, 0, 512, 0]),
@@ -145,6 +153,10 @@ PREFILL_CASES = [
     (8, 2, 128, 1, "bf16", [17, 5], [3, 0]),
     # 512-key blocks; 16 query heads per KV head
     (16, 1, 128, 512, "bf16", [1100, 513, 40], [512, 0, 39]),
+    # 64 sequences (the most the kernel numbers by existing row blocks) and 70 (numbered over the whole grid),
+    # short mixed prompts, some after a cached prefix
+    (8, 2, 128, 16, "bf16", *_short_prompts(11, 64)),
+    (8, 2, 128, 16, "bf16", *_short_prompts(13, 70)),
 ]
 
 
