@@ -157,6 +157,8 @@ PREFILL_CASES = [
     # short mixed prompts, some after a cached prefix
     (8, 2, 128, 16, "bf16", *_short_prompts(11, 64)),
     (8, 2, 128, 16, "bf16", *_short_prompts(13, 70)),
+    # a prompt of more than 63 x 128 rows (numbered over the whole grid as well) after a cached prefix
+    (8, 2, 128, 256, "bf16", [8500], [300]),
 ]
 
 
