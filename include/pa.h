@@ -203,9 +203,12 @@ pa_status pa_norm_rope_store_kvcache(const void* k, int64_t k_tok_stride, const 
  * FlashAttention's varlen ones ("Nano-vLLM 架构详解" §3.2, Attention 运算: Q (total_q, nheads, headdim), cache
  * (num_blocks, page_block_size, nheads_k, headdim), cu_seqlens (batch+1,), max_seqlen, block_tables).
  *   q            (device) [total_q, num_heads, head_dim]; token i starts at element i * q_tok_stride
- *   cu_seqlens_q, cu_seqlens_k (device) [batch+1]
+ *   cu_seqlens_q, cu_seqlens_k (device) [batch+1], cu_seqlens_q[0] = 0 and cu_seqlens_q[batch] = total_q
  *   block_table  (device) [batch, max_blocks_per_seq]
- *   max_seqlen_q (host) >= every q_len; max_seqlen_k (host) >= every k_len (sizes the grid)
+ *   max_seqlen_q (host) >= every q_len; max_seqlen_k (host) >= every k_len; with total_q they size the grid
+ *                (for up to 64 sequences the grid counts the row blocks total_q can hold, so a total_q below
+ *                cu_seqlens_q[batch] would leave rows uncomputed: it is a contract violation, as a q shorter
+ *                than the rows cu_seqlens_q names is)
  *   out          (device) [total_q, num_heads, head_dim], contiguous, out_dtype
  *   workspace    (device) at least pa_prefill_workspace_bytes(...) bytes (may be NULL when that is 0)
  * With few query tiles over long keys (a small chunk after a long cached prefix, as in chunked prefill: fewer
