@@ -47,8 +47,48 @@ __device__ __forceinline__ int64_t stream_chunk(int64_t total, int32_t n_workers
 #endif
 constexpr int kStreamNBuf = PA_STREAM_NBUF;
 
+// Scans and reductions over the 64 lanes by DPP register moves (with an LDS permute per step, a six-step scan is
+// about 700 clocks of dependent latency): an inclusive scan with row shifts of 1, 2, 4 and 8 inside each row of 16
+// lanes, then the row broadcasts of lanes 15 and 31. Lanes a move has no source for take the operation's
+// identity; the reductions return lane 63's total to every lane.
+#define PA_DPP(id, x, ctrl, rmask) __builtin_amdgcn_update_dpp((id), (x), (ctrl), (rmask), 0xf, false)
+__device__ __forceinline__ int dpp_incl_scan_i(int v) {
+  v += PA_DPP(0, v, 0x111, 0xf);
+  v += PA_DPP(0, v, 0x112, 0xf);
+  v += PA_DPP(0, v, 0x114, 0xf);
+  v += PA_DPP(0, v, 0x118, 0xf);
+  v += PA_DPP(0, v, 0x142, 0xa);
+  v += PA_DPP(0, v, 0x143, 0xc);
+  return v;
+}
+__device__ __forceinline__ int dpp_sum_i(int v) { return __builtin_amdgcn_readlane(dpp_incl_scan_i(v), 63); }
+__device__ __forceinline__ float dpp_sum_f(float x) {
+  int v = __float_as_int(x);
+  const int z = __float_as_int(0.f);
+  v = __float_as_int(__int_as_float(v) + __int_as_float(PA_DPP(z, v, 0x111, 0xf)));
+  v = __float_as_int(__int_as_float(v) + __int_as_float(PA_DPP(z, v, 0x112, 0xf)));
+  v = __float_as_int(__int_as_float(v) + __int_as_float(PA_DPP(z, v, 0x114, 0xf)));
+  v = __float_as_int(__int_as_float(v) + __int_as_float(PA_DPP(z, v, 0x118, 0xf)));
+  v = __float_as_int(__int_as_float(v) + __int_as_float(PA_DPP(z, v, 0x142, 0xa)));
+  v = __float_as_int(__int_as_float(v) + __int_as_float(PA_DPP(z, v, 0x143, 0xc)));
+  return __int_as_float(__builtin_amdgcn_readlane(v, 63));
+}
+__device__ __forceinline__ float dpp_max_f(float x) {
+  int v = __float_as_int(x);
+  const int ninf = __float_as_int(-INFINITY);
+  v = __float_as_int(fmaxf(__int_as_float(v), __int_as_float(PA_DPP(ninf, v, 0x111, 0xf))));
+  v = __float_as_int(fmaxf(__int_as_float(v), __int_as_float(PA_DPP(ninf, v, 0x112, 0xf))));
+  v = __float_as_int(fmaxf(__int_as_float(v), __int_as_float(PA_DPP(ninf, v, 0x114, 0xf))));
+  v = __float_as_int(fmaxf(__int_as_float(v), __int_as_float(PA_DPP(ninf, v, 0x118, 0xf))));
+  v = __float_as_int(fmaxf(__int_as_float(v), __int_as_float(PA_DPP(ninf, v, 0x142, 0xa))));
+  v = __float_as_int(fmaxf(__int_as_float(v), __int_as_float(PA_DPP(ninf, v, 0x143, 0xc))));
+  return __int_as_float(__builtin_amdgcn_readlane(v, 63));
+}
+#undef PA_DPP
+__device__ __forceinline__ float lane_of(float v, int j) { return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), j)); }
+
 // cum[s] = sum over i < s of the lengths rounded up to 32, lens[s] = the length (LDS; batch <= 4096). Each
-// thread sums a run of sequences, the runs are scanned within each wave with shuffles and across the four waves
+// thread sums a run of sequences, the runs are scanned within each wave by DPP and across the four waves
 // through LDS.
 __device__ __forceinline__ void stream_prefix(const int32_t* __restrict__ ctx_lens, int32_t len_add, int batch,
                                               int32_t* cum, int32_t* lens) {
@@ -64,12 +104,7 @@ __device__ __forceinline__ void stream_prefix(const int32_t* __restrict__ ctx_le
     lens[s] = L;
     sum += (L + 31) & ~31;
   }
-  int32_t inc = sum;  // inclusive scan over the wave
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int32_t v = __shfl_up(inc, off, 64);
-    if (lane >= off) inc += v;
-  }
+  const int32_t inc = dpp_incl_scan_i(sum);  // inclusive scan over the wave
   if (lane == 63) wave_tot[wv] = inc;
   __syncthreads();
   int32_t run = inc - sum;
@@ -305,6 +340,7 @@ __global__ __launch_bounds__(64 * kStreamWaves) __attribute__((amdgpu_waves_per_
 // rows are read eight at a time.
 constexpr int kMergeEager = 8;
 
+
 __global__ __launch_bounds__(64) void decode_stream_merge_kernel(const int32_t* __restrict__ ctx_lens,
                                                                  int32_t len_add, int32_t batch, int32_t Hq,
                                                                  int32_t Hkv, const float* __restrict__ part,
@@ -315,16 +351,14 @@ __global__ __launch_bounds__(64) void decode_stream_merge_kernel(const int32_t* 
   const int g = int(blockIdx.x) - h * G;
   const int s = blockIdx.y;
   const int lane = threadIdx.x;
-  int64_t before = 0, all = 0;
+  // padded lengths sum below 2^31 (a condition of the balanced decode)
+  int before32 = 0, all32 = 0;
   for (int i = lane; i < batch; i += 64) {
     const int32_t Lp = (ctx_lens[i] + len_add + 31) & ~31;
-    all += Lp;
-    if (i < s) before += Lp;
+    all32 += Lp;
+    if (i < s) before32 += Lp;
   }
-  for (int off = 32; off > 0; off >>= 1) {
-    before += __shfl_xor(before, off, 64);
-    all += __shfl_xor(all, off, 64);
-  }
+  const int64_t before = dpp_sum_i(before32), all = dpp_sum_i(all32);
   const int64_t chunk = stream_chunk(all, n_workers / Hkv);
   const int64_t a = before;
   const int64_t b = a + ((ctx_lens[s] + len_add + 31) & ~31);
@@ -345,13 +379,13 @@ __global__ __launch_bounds__(64) void decode_stream_merge_kernel(const int32_t* 
   float lj = lane < n ? part_of(lane)[16 + g] : 0.f;
   float M = mj;
   for (int j = lane + 64; j < n; j += 64) M = fmaxf(M, part_of(j)[g]);
-  M = wave_max(M);
+  M = dpp_max_f(M);
   float wj = lane < n ? exp2f(mj - M) : 0.f;
-  float Ls = wave_sum(wj * lj);
+  float Ls = dpp_sum_f(wj * lj);
   float a0 = 0.f, a1 = 0.f;
 #pragma unroll
   for (int e = 0; e < kMergeEager; ++e) {
-    const float w = __shfl(wj, e, 64);  // zero past n
+    const float w = lane_of(wj, e);  // zero past n
     a0 += w * v[e].x;
     a1 += w * v[e].y;
   }
@@ -361,7 +395,7 @@ __global__ __launch_bounds__(64) void decode_stream_merge_kernel(const int32_t* 
       mj = lane < nb ? part_of(jb + lane)[g] : -INFINITY;
       lj = lane < nb ? part_of(jb + lane)[16 + g] : 0.f;
       wj = lane < nb ? exp2f(mj - M) : 0.f;
-      Ls += wave_sum(wj * lj);
+      Ls += dpp_sum_f(wj * lj);
     }
     int k = jb == 0 ? kMergeEager : 0;
     for (; k + 8 <= nb; k += 8) {
@@ -370,14 +404,14 @@ __global__ __launch_bounds__(64) void decode_stream_merge_kernel(const int32_t* 
       for (int e = 0; e < 8; ++e) r[e] = *reinterpret_cast<const float2*>(part_of(jb + k + e) + 32 + g * 128 + 2 * lane);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const float w = __shfl(wj, k + e, 64);
+        const float w = lane_of(wj, k + e);
         a0 += w * r[e].x;
         a1 += w * r[e].y;
       }
     }
     for (; k < nb; ++k) {
       const float2 r = *reinterpret_cast<const float2*>(part_of(jb + k) + 32 + g * 128 + 2 * lane);
-      const float w = __shfl(wj, k, 64);
+      const float w = lane_of(wj, k);
       a0 += w * r.x;
       a1 += w * r.y;
     }
