@@ -77,8 +77,8 @@ def algorithmic_work(wl, step, out_bytes: int):
 
 # Sources of the attention kernels each workload kind runs, and the kernels of one attention call: a traffic
 # summary taken on other sources is stale and not reported.
-ATTN_SOURCES = {"decode": ("pa_decode_stream.hip", "pa_decode_tile.h", "pa_common.h", "pa_api.hip"),
-                "prefill": ("pa_prefill.hip", "pa_prefill_tile.h", "pa_common.h", "pa_api.hip")}
+ATTN_SOURCES = {"decode": ("pa_decode_stream.hip", "pa_decode_tile.h", "pa_dpp.h", "pa_common.h", "pa_api.hip"),
+                "prefill": ("pa_prefill.hip", "pa_prefill_tile.h", "pa_dpp.h", "pa_common.h", "pa_api.hip")}
 ATTN_KERNELS = {"decode": ("decode_stream_kernel", "decode_stream_merge_kernel"),
                 "prefill": ("prefill_mfma_kernel", "prefill_merge_kernel")}
 ATTN_KERNELS_OPTIONAL = {"prefill_merge_kernel"}  # launched only by calls that split their keys
@@ -611,7 +611,7 @@ def store_profile(iters: int = 20):
 
 STORE_KERNELS = ("store_kvcache_kernel", "metadata_store_kernel")
 COPY_KERNEL = "MulFunctor"  # torch.mul over 1 GiB of fp16: the plain copy the byte counters are scaled by
-STORE_SOURCES = ("pa_meta_store.hip", "pa_common.h", "pa_api.hip")
+STORE_SOURCES = ("pa_meta_store.hip", "pa_dpp.h", "pa_common.h", "pa_api.hip")
 
 
 def _kernel_calls(path: str, names):

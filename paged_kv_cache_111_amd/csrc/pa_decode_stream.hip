@@ -23,6 +23,7 @@
 // lengths and the per-wave fixed costs of short ones. The per-tile work (32-key tiles of K and V through buffer
 // descriptors, 16x16x32 bf16 MFMAs for scores and PV, online softmax) is the split kernel's.
 #include "pa_decode_tile.h"
+#include "pa_dpp.h"
 
 namespace pa {
 
@@ -46,46 +47,6 @@ __device__ __forceinline__ int64_t stream_chunk(int64_t total, int32_t n_workers
 #define PA_STREAM_NBUF 1
 #endif
 constexpr int kStreamNBuf = PA_STREAM_NBUF;
-
-// Scans and reductions over the 64 lanes by DPP register moves (with an LDS permute per step, a six-step scan is
-// about 700 clocks of dependent latency): an inclusive scan with row shifts of 1, 2, 4 and 8 inside each row of 16
-// lanes, then the row broadcasts of lanes 15 and 31. Lanes a move has no source for take the operation's
-// identity; the reductions return lane 63's total to every lane.
-#define PA_DPP(id, x, ctrl, rmask) __builtin_amdgcn_update_dpp((id), (x), (ctrl), (rmask), 0xf, false)
-__device__ __forceinline__ int dpp_incl_scan_i(int v) {
-  v += PA_DPP(0, v, 0x111, 0xf);
-  v += PA_DPP(0, v, 0x112, 0xf);
-  v += PA_DPP(0, v, 0x114, 0xf);
-  v += PA_DPP(0, v, 0x118, 0xf);
-  v += PA_DPP(0, v, 0x142, 0xa);
-  v += PA_DPP(0, v, 0x143, 0xc);
-  return v;
-}
-__device__ __forceinline__ int dpp_sum_i(int v) { return __builtin_amdgcn_readlane(dpp_incl_scan_i(v), 63); }
-__device__ __forceinline__ float dpp_sum_f(float x) {
-  int v = __float_as_int(x);
-  const int z = __float_as_int(0.f);
-  v = __float_as_int(__int_as_float(v) + __int_as_float(PA_DPP(z, v, 0x111, 0xf)));
-  v = __float_as_int(__int_as_float(v) + __int_as_float(PA_DPP(z, v, 0x112, 0xf)));
-  v = __float_as_int(__int_as_float(v) + __int_as_float(PA_DPP(z, v, 0x114, 0xf)));
-  v = __float_as_int(__int_as_float(v) + __int_as_float(PA_DPP(z, v, 0x118, 0xf)));
-  v = __float_as_int(__int_as_float(v) + __int_as_float(PA_DPP(z, v, 0x142, 0xa)));
-  v = __float_as_int(__int_as_float(v) + __int_as_float(PA_DPP(z, v, 0x143, 0xc)));
-  return __int_as_float(__builtin_amdgcn_readlane(v, 63));
-}
-__device__ __forceinline__ float dpp_max_f(float x) {
-  int v = __float_as_int(x);
-  const int ninf = __float_as_int(-INFINITY);
-  v = __float_as_int(fmaxf(__int_as_float(v), __int_as_float(PA_DPP(ninf, v, 0x111, 0xf))));
-  v = __float_as_int(fmaxf(__int_as_float(v), __int_as_float(PA_DPP(ninf, v, 0x112, 0xf))));
-  v = __float_as_int(fmaxf(__int_as_float(v), __int_as_float(PA_DPP(ninf, v, 0x114, 0xf))));
-  v = __float_as_int(fmaxf(__int_as_float(v), __int_as_float(PA_DPP(ninf, v, 0x118, 0xf))));
-  v = __float_as_int(fmaxf(__int_as_float(v), __int_as_float(PA_DPP(ninf, v, 0x142, 0xa))));
-  v = __float_as_int(fmaxf(__int_as_float(v), __int_as_float(PA_DPP(ninf, v, 0x143, 0xc))));
-  return __int_as_float(__builtin_amdgcn_readlane(v, 63));
-}
-#undef PA_DPP
-__device__ __forceinline__ float lane_of(float v, int j) { return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), j)); }
 
 // cum[s] = sum over i < s of the lengths rounded up to 32, lens[s] = the length (LDS; batch <= 4096). Each
 // thread sums a run of sequences, the runs are scanned within each wave by DPP and across the four waves

@@ -4,6 +4,7 @@
 // delimit sequences ("一个 prompt 的一生" §3.3.2, prepare_prefill example; slot formula of "Nano-vLLM 架构详解"
 // §1, Step2). Store: a bit copy of each new token's K/V row to its slot ("Nano-vLLM 架构详解" §3.2, KV cache
 // 写入函数).
+#include "pa_dpp.h"
 #include "pa_launch.h"
 
 namespace pa {
@@ -34,17 +35,8 @@ __device__ __forceinline__ void meta_prefix_sums(const int32_t* __restrict__ num
     sq += n;
     sk += num_cached[s] + n;
   }
-  // exclusive prefix of the per-thread sums: inclusive scan within each wave by shuffles, then across the waves
-  int32_t iq = sq, ik = sk;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int32_t vq = __shfl_up(iq, off, 64);
-    const int32_t vk = __shfl_up(ik, off, 64);
-    if (lane >= off) {
-      iq += vq;
-      ik += vk;
-    }
-  }
+  // exclusive prefix of the per-thread sums: inclusive scan within each wave (DPP), then across the waves
+  const int32_t iq = dpp_incl_scan_i(sq), ik = dpp_incl_scan_i(sk);
   if (lane == 63) {
     wave_q[wave] = iq;
     wave_k[wave] = ik;

@@ -33,6 +33,7 @@
 #include <algorithm>
 #include <type_traits>
 
+#include "pa_dpp.h"
 #include "pa_prefill_tile.h"
 
 namespace pa {
@@ -327,12 +328,12 @@ __global__ __launch_bounds__(64) void prefill_merge_kernel(const int32_t* __rest
   const float* p = part + ((int64_t(a) * part_rows + r) * Hq + h) * n_splits * kPartRow;
   const float mj = lane < n_splits ? p[lane * kPartRow] : -INFINITY;
   const float lj = lane < n_splits ? p[lane * kPartRow + 1] : 0.f;
-  const float M = wave_max(mj);  // split 0 holds key 0, which every row sees: M is finite
+  const float M = dpp_max_f(mj);  // split 0 holds key 0, which every row sees: M is finite
   const float wj = mj == -INFINITY ? 0.f : exp2f(mj - M);
-  const float L = wave_sum(wj * lj);
+  const float L = dpp_sum_f(wj * lj);
   float a0 = 0.f, a1 = 0.f;
   for (int j = 0; j < n_splits; ++j) {
-    const float w = __shfl(wj, j, 64);
+    const float w = lane_of(wj, j);
     if (w != 0.f) {  // wave-uniform; a split without keys for the row left no O
       const float2 v = *reinterpret_cast<const float2*>(p + j * kPartRow + 4 + 2 * lane);
       a0 += w * v.x;
