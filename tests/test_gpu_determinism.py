@@ -1,4 +1,5 @@
-"""Repeated calls on the same inputs give bit-identical outputs (the measured workloads at full size).
+"""Repeated calls on the same inputs give bit-identical outputs (the measured workloads at full size), also when
+calls run concurrently on two streams.
 
 An engine that replays a step, or compares two runs of a request, needs the attention output to depend only on
 the inputs: the kernels use no atomics in their arithmetic, the balanced decode's work division and the prefill
@@ -64,3 +65,39 @@ def test_decode_step_repeats_bit_for_bit(name):
             ctx = i32(np.asarray(st.num_cached) + 1)
             pa.decode(ds.q, kc, vc, ctx, ds.block_table, wl.scale, workspace=ws)
     assert np.array_equal(outs[0], outs[1]) and np.array_equal(outs[0], outs[2]), f"{name}: outputs differ"
+
+
+@pytest.mark.gpu
+def test_calls_on_two_streams_match_the_calls_alone():
+    """The library keeps no state between calls but the caller's buffers: a decode step and a varlen prefill
+    enqueued on two streams at once (each with its own pools and workspace) give the bits they give alone."""
+    dec, pre = make_config("decode_qwen3_0p6b"), make_config("prefill_qwen3_8b")
+    sd, sp = dec.steps[-1], pre.steps[-1]
+    dkc, dvc = to_dev(dec.k_cache, dec.dtype), to_dev(dec.v_cache, dec.dtype)
+    pkc, pvc = to_dev(pre.k_cache, pre.dtype), to_dev(pre.v_cache, pre.dtype)
+    dds, pds = DevStep(sd, dec.dtype), DevStep(sp, pre.dtype)
+    meta = pa.build_metadata_store(pds.num_cached, pds.num_new, pds.block_table, pds.total_q, pds.k, pds.v, pkc, pvc)
+    mbps = int(sd.block_table.shape[1])
+    dws = torch.empty(pa.decode_workspace_bytes(sd.batch, dec.num_heads, dec.num_kv_heads, dec.head_dim, mbps,
+                                                dec.block_size, 0), dtype=torch.uint8, device=DEV)
+
+    def run_decode(stream=None):
+        return pa.decode_append(dds.q, dds.k, dds.v, dkc, dvc, dds.num_cached, dds.block_table, dec.scale,
+                                workspace=dws, fallback=False, stream=stream)
+
+    def run_prefill(stream=None):
+        return pa.prefill_varlen(pds.q, pkc, pvc, meta["cu_seqlens_q"], meta["cu_seqlens_k"], pds.block_table,
+                                 pds.max_q, pds.max_k, pre.scale, stream=stream)
+
+    alone_d = _bits(run_decode())
+    alone_p = _bits(run_prefill())
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()  # default priority
+    for _ in range(3):
+        torch.cuda.synchronize()
+        with torch.cuda.stream(s1):
+            od = run_decode(stream=s1)
+        with torch.cuda.stream(s2):
+            op = run_prefill(stream=s2)
+        torch.cuda.synchronize()
+        assert np.array_equal(_bits(od), alone_d), "decode on a second stream differs"
+        assert np.array_equal(_bits(op), alone_p), "prefill on a second stream differs"
